@@ -1,0 +1,339 @@
+"""Plain, slow, fp64 CPU oracle for the forward pass of one mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module: only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or call it. It shares no code with the HIP library and imports nothing from
+the package; callers hand it plain NumPy arrays (bf16 inputs already widened to float).
+
+Every value is computed in float64 from the exact stored input values, with no
+intermediate rounding. Each step cites the passage of the source pages it follows:
+
+* p1 = "Section 21: Merging Routed and Shared Expert Activations" (Olmo-core MoE report)
+* p2 = "Appendix E: Expert-Merge Normalization in Public MoE Models"
+* p3 = "Shared and Fine-Grained Experts" (AI wiki entry with a PyTorch listing)
+* p4 = "Section 20: One Shared Expert Is All You Need"
+* p5 = "Section 10: Routing, Capacity, and Load Balancing"
+
+Weights use the layout of a PyTorch ``Linear.weight``: the pages write the SwiGLU expert
+in row-vector form, E(x) = [SiLU(x W_g) * (x W_u)] W_d (p4, Eq. 74); here
+``w_gate = W_g^T`` with shape [d_ff, d_model], ``w_up = W_u^T`` [d_ff, d_model] and
+``w_down = W_d^T`` [d_model, d_ff].
+
+Readings taken where the pages leave a step open (each is listed in the design doc):
+  * top-K ties go to the lower expert index; -0.0 and +0.0 compare equal;
+  * the K output slots of a token are ordered by descending key, ties by index;
+  * selection uses the (biased) logit for every score function;
+  * without renormalization the routed coefficient is alpha * q_i;
+  * per-expert capacity keeps the first `capacity` routes in token-index order;
+  * kept segments are laid out in ascending expert order, rows by ascending token.
+Parity pins for every function live in tests/test_oracle_pins.py; no function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+SOFTMAX = 0            # softmax over all N logits (p1 Eq. 83 with renorm; p2 Qwen/OLMoE rows without)
+SIGMOID = 1            # sigmoid affinities (p2 Table 52, DeepSeek-V3 row)
+SOFTMAX_SELECTED = 2   # softmax over the K selected logits only (p2 Table 52, Mixtral row)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _sigmoid(v: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-v))
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v), the gate nonlinearity of SwiGLU (p4 Eq. 74)."""
+    return _f64(v) * _sigmoid(_f64(v))
+
+
+# ----------------------------------------------------------------------------------------
+# a1: router logits
+# ----------------------------------------------------------------------------------------
+def router_logits(x, w_router, logit_bias=None) -> np.ndarray:
+    """z = x W_r^T (+ b): the bias-free router projection of the p3 listing (`gate`,
+    a Linear from d_model to n_routed without bias; "Router projection and gating
+    function" in p5 Table 16). An optional per-expert bias b is added to every logit."""
+    z = _f64(x) @ _f64(w_router).T
+    if logit_bias is not None:
+        z = z + _f64(logit_bias)[None, :]
+    return z
+
+
+def shared_gate(x, w_shared_gate) -> np.ndarray:
+    """s(x) = sigmoid(x w_s): the learned sigmoid shared-expert gate (p2 Table 52,
+    Qwen rows), one scalar per token from a d_model-vector."""
+    return _sigmoid(_f64(x) @ _f64(w_shared_gate))
+
+
+# ----------------------------------------------------------------------------------------
+# a2: selection and routed coefficients
+# ----------------------------------------------------------------------------------------
+def topk_select(keys, K: int) -> np.ndarray:
+    """S(x): the K experts whose keys outrank every unselected expert (p1 Eq. 80 with
+    |S| = K; p5 Section 10.7.1 ordering constraint). Ties go to the lower index, and
+    the slots come out by descending key, then ascending index. The comparison is done
+    in the precision of `keys` (pass float32 logits to decide in float32)."""
+    keys = np.asarray(keys)
+    T, N = keys.shape
+    if not (1 <= K <= N):
+        raise ValueError("need 1 <= K <= N")
+    neg = -keys
+    neg = np.where(neg == 0, np.zeros_like(neg), neg)  # -0.0 and +0.0 are the same key
+    index = np.broadcast_to(np.arange(N), (T, N))
+    order = np.lexsort((index, neg), axis=-1)        # primary: -key, secondary: index
+    return order[:, :K].astype(np.int32)
+
+
+def route_coefficients(z, idx, score: int, renorm: bool, alpha: float) -> np.ndarray:
+    """r_{t,k} for the selected experts.
+
+    * SOFTMAX: q = softmax over all N logits; with renorm p_i = q_i / sum_S q_j and
+      r_i = alpha p_i (p1 Eq. 83 for alpha = K; p2 Appendix E), without renorm
+      r_i = alpha q_i, whose routed mass m_K = sum_S q_i < 1 (p2 Qwen1.5/2, OLMoE rows).
+    * SIGMOID: selected sigmoid affinities, renormalized and scaled by alpha
+      (p2 Table 52, DeepSeek-V3 row, alpha = 2.5).
+    * SOFTMAX_SELECTED: softmax over the selected logits only, times alpha
+      (p2 Table 52, Mixtral row; p3 closing paragraph).
+    """
+    z = _f64(z)
+    zS = np.take_along_axis(z, idx.astype(np.int64), axis=1)
+    if score == SOFTMAX:
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        q = e / e.sum(axis=1, keepdims=True)
+        qS = np.take_along_axis(q, idx.astype(np.int64), axis=1)
+        p = qS / qS.sum(axis=1, keepdims=True) if renorm else qS
+    elif score == SIGMOID:
+        a = _sigmoid(zS)
+        p = a / a.sum(axis=1, keepdims=True) if renorm else a
+    elif score == SOFTMAX_SELECTED:
+        m = zS.max(axis=1, keepdims=True)
+        e = np.exp(zS - m)
+        p = e / e.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(f"unknown score function {score}")
+    return float(alpha) * p
+
+
+# ----------------------------------------------------------------------------------------
+# a3: requested and kept counts, capacity, offsets, restoration map
+# ----------------------------------------------------------------------------------------
+def requested_counts(idx, N: int) -> np.ndarray:
+    """C_i^req = number of tokens whose selected set contains i (p5 Eq. 19)."""
+    return np.bincount(np.asarray(idx).reshape(-1), minlength=N).astype(np.int64)
+
+
+def capacity_from_factor(c: float, K: int, T: int, N: int) -> int:
+    """Independent per-expert capacity ceil(c T_route / N_local) (p5 Eq. 25), with
+    T_route = K T routes from the one source and N_local = N experts."""
+    return int(math.ceil(float(c) * K * T / N))
+
+
+def keep_routes(idx, N: int, capacity: int) -> np.ndarray:
+    """Kept-route mask under per-expert first-come capacity: scanning tokens in index
+    order, route (t, i) is admitted while fewer than `capacity` routes to expert i have
+    been admitted (p5 Eq. 21 kept vs dropped; Eq. 25 per-expert limit). A negative
+    capacity means unlimited (every requested route is kept)."""
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    kept = np.zeros((T, K), dtype=bool)
+    used = np.zeros(N, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            if capacity < 0 or used[e] < capacity:
+                kept[t, k] = True
+                used[e] += 1
+    return kept
+
+
+@dataclass
+class Permutation:
+    C_keep: np.ndarray        # [N]   M_i, rows presented to expert i (p5 Eq. 21)
+    offsets: np.ndarray       # [N+1] o_0 = 0, o_{i+1} = o_i + M_i (p5 Eq. 26)
+    dest_row: np.ndarray      # [T,K] packed row of each kept route, -1 when dropped
+    row_token: np.ndarray     # [R]   source token of each packed row
+
+
+def permutation(idx, kept, N: int) -> Permutation:
+    """Pack kept routes into dense per-expert segments: expert i owns rows
+    [o_i, o_{i+1}) with o given by the cumulative kept counts (p5 Eq. 26, "valid rows
+    packed at the front"); inside a segment rows follow ascending token index.
+    Dropped routes get no row and are masked in restoration and combine (p5 Section
+    10.3)."""
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    C_keep = np.bincount(idx[kept].reshape(-1), minlength=N).astype(np.int64)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(C_keep)
+    fill = offsets[:-1].copy()
+    dest = np.full((T, K), -1, dtype=np.int64)
+    row_token = np.zeros(int(offsets[-1]), dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            if kept[t, k]:
+                e = int(idx[t, k])
+                dest[t, k] = fill[e]
+                row_token[fill[e]] = t
+                fill[e] += 1
+    return Permutation(C_keep, offsets, dest, row_token)
+
+
+# ----------------------------------------------------------------------------------------
+# a5-a7: SwiGLU experts
+# ----------------------------------------------------------------------------------------
+def swiglu(X, w_gate, w_up, w_down):
+    """E(X) = [SiLU(X W_g) * (X W_u)] W_d (p4 Eq. 74), with stored-transposed weights.
+    Returns (H, F): the intermediate activation [M, d_ff] and the output [M, d_model]."""
+    X = _f64(X)
+    H = silu(X @ _f64(w_gate).T) * (X @ _f64(w_up).T)
+    return H, H @ _f64(w_down).T
+
+
+def shared_output(x, shared_experts: Sequence) -> Optional[np.ndarray]:
+    """g(x) = sum_j E_j(x) over the ungated shared experts, each evaluated on its own
+    (p4 Eq. 76 left-hand side). Returns None when there is no shared expert."""
+    if not shared_experts:
+        return None
+    g = None
+    for (wg, wu, wd) in shared_experts:
+        _, Fj = swiglu(x, wg, wu, wd)
+        g = Fj if g is None else g + Fj
+    return g
+
+
+# ----------------------------------------------------------------------------------------
+# a8: combine
+# ----------------------------------------------------------------------------------------
+def combine(F_perm, dest_row, r, G=None, s=1.0) -> np.ndarray:
+    """y_t = sum_{i in S_t, kept} r_{t,i} f_i(x_t) + s_t g(x_t) (p1 Eq. 80), reading each
+    expert output from its packed row. Dropped routes contribute nothing and the kept
+    coefficients are not renormalized (p5 Section 10.3: restoration and combine mask
+    the tail-dropped routes). `s` is a scalar gain or a per-token gate vector."""
+    dest_row = np.asarray(dest_row)
+    T, K = dest_row.shape
+    F_perm = _f64(F_perm)
+    d = F_perm.shape[1] if F_perm.ndim == 2 and F_perm.shape[0] else (
+        G.shape[1] if G is not None else 0)
+    y = np.zeros((T, d))
+    r = _f64(r)
+    for k in range(K):
+        m = dest_row[:, k] >= 0
+        if m.any():
+            y[m] += r[m, k, None] * F_perm[dest_row[m, k]]
+    if G is not None:
+        s_arr = _f64(s)
+        y += (s_arr[:, None] if s_arr.ndim == 1 else s_arr) * _f64(G)
+    return y
+
+
+# ----------------------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------------------
+@dataclass
+class LayerSpec:
+    """Arguments of one MoE layer, in the pages' notation."""
+    N: int
+    K: int
+    score: int = SOFTMAX
+    renorm: bool = True
+    alpha: float = 1.0
+    s: float = 1.0                    # fixed shared gain when there is no learned gate
+    capacity: int = -1                # routes kept per expert; < 0 = unlimited
+
+
+@dataclass
+class Result:
+    logits: np.ndarray
+    idx: np.ndarray
+    r: np.ndarray
+    s_tok: Optional[np.ndarray]
+    C_req: np.ndarray
+    kept: np.ndarray
+    perm: Permutation
+    H_perm: np.ndarray
+    F_perm: np.ndarray
+    G: Optional[np.ndarray]
+    y: np.ndarray
+
+
+def forward(spec: LayerSpec, x, w_router, expert_weights: Callable[[int], tuple],
+            shared_experts: Sequence = (), logit_bias=None, w_shared_gate=None,
+            logits_override=None) -> Result:
+    """The whole layer forward, stage by stage (p5 Section 10 opening paragraph:
+    router -> capacity -> dispatch -> grouped expert compute -> combine; p1 Eq. 80).
+
+    `expert_weights(i)` returns (w_gate, w_up, w_down) of routed expert i.
+    `logits_override` (e.g. float32 logits) replaces the computed logits for selection
+    and coefficients, so that near-ties are decided on identical values."""
+    x = _f64(x)
+    T = x.shape[0]
+    z = router_logits(x, w_router, logit_bias)
+    keys = z if logits_override is None else np.asarray(logits_override)
+    idx = topk_select(keys, spec.K)
+    r = route_coefficients(keys, idx, spec.score, spec.renorm, spec.alpha)
+    s_tok = shared_gate(x, w_shared_gate) if w_shared_gate is not None else None
+    C_req = requested_counts(idx, spec.N)
+    kept = keep_routes(idx, spec.N, spec.capacity)
+    perm = permutation(idx, kept, spec.N)
+    R = int(perm.offsets[-1])
+    d = x.shape[1]
+    x_perm = x[perm.row_token] if R else np.zeros((0, d))
+    H_perm = None
+    F_perm = np.zeros((R, d))
+    for i in range(spec.N):
+        a, b = int(perm.offsets[i]), int(perm.offsets[i + 1])
+        if b > a:
+            wg, wu, wd = expert_weights(i)
+            Hi, Fi = swiglu(x_perm[a:b], wg, wu, wd)
+            if H_perm is None:
+                H_perm = np.zeros((R, Hi.shape[1]))
+            H_perm[a:b] = Hi
+            F_perm[a:b] = Fi
+    if H_perm is None:
+        H_perm = np.zeros((R, 0))
+    G = shared_output(x, shared_experts)
+    gain = s_tok if s_tok is not None else spec.s
+    y = combine(F_perm, perm.dest_row, r, G, gain)
+    return Result(z, idx, r, s_tok, C_req, kept, perm, H_perm, F_perm, G, y)
+
+
+def forward_tokens(spec: LayerSpec, tokens, x, idx, r, kept_or_dest, expert_weights,
+                   shared_experts: Sequence = (), s_tok=None) -> np.ndarray:
+    """y for a subset of tokens, one token at a time, given that token's routing
+    (selected experts, coefficients and which routes were kept). This is p1 Eq. 80
+    evaluated directly per token, f_i(x) = E_i(x) of p4 Eq. 74, for sampled checks at
+    sizes where the whole layer is too slow on the CPU."""
+    x = _f64(x)
+    kept = np.asarray(kept_or_dest)
+    if kept.dtype != bool:
+        kept = kept >= 0
+    cache = {}
+    out = []
+    for t in tokens:
+        xt = x[t:t + 1]
+        yt = np.zeros((1, x.shape[1]))
+        for k in range(idx.shape[1]):
+            if kept[t, k]:
+                e = int(idx[t, k])
+                if e not in cache:
+                    cache.clear()
+                    cache[e] = expert_weights(e)
+                _, Fe = swiglu(xt, *cache[e])
+                yt += float(r[t, k]) * Fe
+        g = shared_output(xt, shared_experts)
+        if g is not None:
+            gain = float(s_tok[t]) if s_tok is not None else spec.s
+            yt += gain * g
+        out.append(yt[0])
+    return np.stack(out) if out else np.zeros((0, x.shape[1]))

@@ -1,0 +1,481 @@
+"""Pins for the CPU oracle against facts fixed by the pages and by mathematics.
+
+Every check here is independent of the oracle's own formulas: worked examples printed on
+the pages (tests/golden/), closed forms, invariants, brute force on tiny inputs, and
+textbook computations (a dense SwiGLU MLP, a pure-Python matmul). The mutation tests at
+the end plant plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+from mixture_experts_layer_gemm_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------------------
+# helpers written from the textbook definitions, not from the oracle
+# --------------------------------------------------------------------------------------
+def py_matmul_nt(a, b):
+    """Pure-Python a @ b.T with math.fsum accumulation."""
+    return [[math.fsum(a[i][k] * b[j][k] for k in range(len(a[i]))) for j in range(len(b))]
+            for i in range(len(a))]
+
+
+def dense_swiglu(x, wg, wu, wd):
+    """A plain dense SwiGLU MLP, y = (silu(x Wg^T) * (x Wu^T)) Wd^T, silu(v) = v/(1+e^-v)."""
+    a = x @ wg.T
+    return ((a / (1.0 + np.exp(-a))) * (x @ wu.T)) @ wd.T
+
+
+def brute_topk(keys, K):
+    """All K-subsets whose every member outranks every non-member; among them the one
+    with the lowest indices (lowest-index tie break), slots by (-key, index)."""
+    N = len(keys)
+    best = None
+    for S in itertools.combinations(range(N), K):
+        rest = [j for j in range(N) if j not in S]
+        if rest and min(keys[i] for i in S) < max(keys[j] for j in rest):
+            continue
+        if best is None or tuple(sorted(S)) < tuple(sorted(best)):
+            best = S
+    return sorted(best, key=lambda i: (-keys[i], i))
+
+
+def eq85_ratio(d_r, d_s, r, s):
+    """Eq. 85 of p1: variance ratio of the MoE to the matched dense MLP."""
+    return (d_r * sum(v * v for v in r) + d_s * s * s) / (len(r) * d_r + d_s)
+
+
+def small_layer(seed=0, T=64, d=32, N=8, K=2, dr=24, shared=(16,), std=0.3, zero_router=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = np.zeros((N, d)) if zero_router else rng.standard_normal((N, d)) * std
+    experts = [(rng.standard_normal((dr, d)) * std, rng.standard_normal((dr, d)) * std,
+                rng.standard_normal((d, dr)) * std) for _ in range(N)]
+    sh = [(rng.standard_normal((m, d)) * std, rng.standard_normal((m, d)) * std,
+           rng.standard_normal((d, m)) * std) for m in shared]
+    return x, wr, experts, sh
+
+
+# --------------------------------------------------------------------------------------
+# a1 logits
+# --------------------------------------------------------------------------------------
+def test_logits_match_pure_python_matmul():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 17))
+    w = rng.standard_normal((6, 17))
+    b = rng.standard_normal(6)
+    ref = py_matmul_nt(x.tolist(), w.tolist())
+    z = O.router_logits(x, w, b)
+    for i in range(5):
+        for j in range(6):
+            assert abs(z[i, j] - (ref[i][j] + b[j])) <= 1e-12 * (1 + abs(ref[i][j]))
+
+
+def test_logits_on_bf16_slices_of_every_workload():
+    for name in ["C0", "S_softmax", "S_sigmoid"]:
+        cfg = synth.get_config(name)
+        inp = synth.make_inputs(cfg, T=4) if cfg.T >= 4 else synth.make_inputs(cfg)
+        x = inp.as_float(inp.x)[:3].astype(np.float64)
+        w = inp.as_float(inp.w_router).astype(np.float64)
+        ref = py_matmul_nt(x.tolist(), w.tolist())
+        z = O.router_logits(x, w)
+        assert np.max(np.abs(z - np.array(ref))) <= 1e-12
+
+
+# --------------------------------------------------------------------------------------
+# a2 selection
+# --------------------------------------------------------------------------------------
+def test_topk_brute_force_with_forced_ties():
+    rng = np.random.default_rng(2)
+    for trial in range(1500):
+        N = int(rng.integers(1, 9))
+        K = int(rng.integers(1, min(N, 4) + 1))
+        keys = rng.integers(-2, 3, size=N).astype(np.float32)  # many ties
+        got = O.topk_select(keys[None, :], K)[0].tolist()
+        assert got == brute_topk(keys.tolist(), K), (keys, K)
+
+
+def test_topk_negative_zero_ties_positive_zero():
+    keys = np.array([[-0.0, 0.0, -1.0]], dtype=np.float32)
+    assert O.topk_select(keys, 1).tolist() == [[0]]
+    keys = np.array([[0.0, -0.0, -1.0]], dtype=np.float32)
+    assert O.topk_select(keys, 2).tolist() == [[0, 1]]
+
+
+def test_topk_all_equal_and_k_equals_n():
+    z = np.zeros((3, 7))
+    assert O.topk_select(z, 3).tolist() == [[0, 1, 2]] * 3
+    z = np.random.default_rng(3).standard_normal((4, 5))
+    got = O.topk_select(z, 5)
+    assert all(sorted(row) == [0, 1, 2, 3, 4] for row in got.tolist())
+
+
+def test_fig69_olmo_rule_worked_example():
+    g = golden("fig69_merge_example.json")
+    p = np.array(g["p"])
+    z = np.log(p)[None, :]                         # softmax(ln p) = p since sum p = 1
+    idx = O.topk_select(z, g["K"])
+    r = O.route_coefficients(z, idx, O.SOFTMAX, True, float(g["K"]))
+    r_by_expert = np.zeros(4)
+    r_by_expert[idx[0]] = r[0]
+    assert np.allclose(r_by_expert, g["r"], atol=1e-12)
+    assert abs(r.sum() - g["sum_r"]) < 1e-12
+    a_w = (g["d_r"] * r.sum() + g["d_s"] * g["s"]) / (g["K"] * g["d_r"] + g["d_s"])
+    assert abs(a_w - g["a_w"]) < 1e-12
+    assert abs(np.sum(p ** 2) - g["sum_p2"]) < 1e-12
+    assert abs(eq85_ratio(g["d_r"], g["d_s"], r_by_expert, g["s"]) - g["R_var"]) < 5e-4
+    assert g["K"] * g["d_r"] + g["d_s"] == g["d_act"]
+
+
+def test_coefficient_sums_per_mode():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((200, 16)) * 2
+    idx = O.topk_select(z, 4)
+    # Olmo rule: selected normalization then alpha = K, so sum_i r_i = K (p1 Eq. 83)
+    assert np.allclose(O.route_coefficients(z, idx, O.SOFTMAX, True, 4.0).sum(1), 4.0)
+    # renormalized sigmoid affinities times alpha = 2.5 sum to 2.5 (p2 DeepSeek-V3 row)
+    assert np.allclose(O.route_coefficients(z, idx, O.SIGMOID, True, 2.5).sum(1), 2.5)
+    # softmax over the selected logits: routed mass one (p2 Mixtral row)
+    assert np.allclose(O.route_coefficients(z, idx, O.SOFTMAX_SELECTED, False, 1.0).sum(1), 1.0)
+    # full softmax without renormalization: routed mass m_K < 1 (p2 Qwen / OLMoE rows)
+    r = O.route_coefficients(z, idx, O.SOFTMAX, False, 1.0)
+    e = np.exp(z - z.max(1, keepdims=True))
+    q = e / e.sum(1, keepdims=True)
+    assert np.all(r.sum(1) < 1.0)
+    assert np.allclose(r, np.take_along_axis(q, idx, 1), atol=1e-15)
+    # unrenormalized sigmoid: each coefficient is alpha * sigma(z_i)
+    r = O.route_coefficients(z, idx, O.SIGMOID, False, 2.0)
+    assert np.allclose(r, 2.0 / (1 + np.exp(-np.take_along_axis(z, idx, 1))), atol=1e-15)
+
+
+def test_selected_softmax_equals_renormalized_softmax():
+    # exp(z_i)/sum_S exp(z_j) == q_i / sum_S q_j in exact arithmetic (p3's "nearly the same")
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((100, 8)) * 3
+    idx = O.topk_select(z, 2)
+    a = O.route_coefficients(z, idx, O.SOFTMAX_SELECTED, True, 1.0)
+    b = O.route_coefficients(z, idx, O.SOFTMAX, True, 1.0)
+    assert np.max(np.abs(a - b)) < 1e-14
+
+
+def test_selected_outrank_unselected():
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((300, 32)).astype(np.float32)
+    idx = O.topk_select(z, 8)
+    for t in range(300):
+        S = set(idx[t].tolist())
+        worst_sel = min(z[t, i] for i in S)
+        best_uns = max(z[t, j] for j in range(32) if j not in S)
+        assert worst_sel >= best_uns
+        keys = [z[t, i] for i in idx[t]]
+        assert keys == sorted(keys, reverse=True)
+
+
+def test_shared_gate_is_sigmoid_of_projection():
+    x = np.array([[1.0, -2.0], [0.0, 0.0]])
+    w = np.array([0.5, 0.25])
+    assert np.allclose(O.shared_gate(x, w), [0.5, 0.5])
+
+
+def test_silu_values():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(O.silu(np.array([-40.0]))[0]) < 1e-15
+    assert O.silu(np.array([-1000.0]))[0] == 0.0
+
+
+# --------------------------------------------------------------------------------------
+# a3 counts, capacity, offsets
+# --------------------------------------------------------------------------------------
+def test_requested_counts_sum_to_KT():
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal((513, 64))
+    idx = O.topk_select(z, 4)
+    C = O.requested_counts(idx, 64)
+    assert C.sum() == 4 * 513                         # p5 Eq. 19
+    brute = [sum(1 for t in range(513) if i in idx[t]) for i in range(64)]
+    assert C.tolist() == brute
+
+
+def test_capacity_formula():
+    assert O.capacity_from_factor(1.0, 4, 4096, 64) == 256    # 4 * 4096 / 64
+    assert O.capacity_from_factor(1.0, 4, 600, 16) == 150
+    assert O.capacity_from_factor(0.5, 4, 600, 16) == 75
+    assert O.capacity_from_factor(1.25, 2, 10, 3) == 9        # ceil(8.33)
+    assert O.capacity_from_factor(1.0, 1, 1, 64) == 1
+
+
+def test_fig41_per_expert_capacity():
+    g = golden("fig41_capacity_example.json")
+    b = g["per_expert_limit_b"]
+    # top-1 routes, experts interleaved in token order: E0 x5, E1 x1, E2 x3, E3 x3
+    order = [0, 2, 0, 3, 0, 1, 0, 2, 3, 0, 2, 3]
+    idx = np.array(order, dtype=np.int32)[:, None]
+    req = O.requested_counts(idx, 4)
+    assert req.tolist() == [g["requests"][f"E{i}"] for i in range(4)]
+    kept = O.keep_routes(idx, 4, b)
+    perm = O.permutation(idx, kept, 4)
+    assert int(kept.sum()) == g["per_expert"]["kept"]
+    dropped = (req - perm.C_keep).tolist()
+    assert dropped == g["per_expert"]["dropped_by_expert"]
+    assert sum(dropped) == g["per_expert"]["dropped"]
+    assert 4 * b - perm.C_keep.sum() == g["per_expert"]["unused_rows"]
+    # first come by token index: expert 0 keeps its first three tokens (0, 2, 4)
+    assert [t for t in range(12) if order[t] == 0 and kept[t, 0]] == [0, 2, 4]
+    # drop fraction, p5 Eq. 27
+    assert sum(dropped) / req.sum() == pytest.approx(2 / 12)
+    # Eq. 28-29: a shared rank-wide budget B drops no more than per-expert budgets b
+    B = g["rows_per_rank_B"]
+    d_rank = sum(max(req[2 * q] + req[2 * q + 1] - B, 0) for q in range(2))
+    assert d_rank == g["rank_wide"]["dropped"] and d_rank <= sum(dropped)
+
+
+def test_keep_closed_form_and_permutation_invariants():
+    rng = np.random.default_rng(8)
+    T, N, K = 700, 16, 4
+    bias = synth.zipf_logit_bias(N).astype(np.float64)
+    z = rng.standard_normal((T, N)) + bias
+    idx = O.topk_select(z, K)
+    for cap in [-1, 0, 1, 37, 175, 10_000]:
+        kept = O.keep_routes(idx, N, cap)
+        req = O.requested_counts(idx, N)
+        perm = O.permutation(idx, kept, N)
+        expect = req if cap < 0 else np.minimum(req, cap)
+        assert perm.C_keep.tolist() == expect.tolist()          # closed form of first-come
+        assert perm.offsets[0] == 0 and perm.offsets[-1] == perm.C_keep.sum()   # Eq. 26
+        assert np.all(np.diff(perm.offsets) == perm.C_keep)
+        R = perm.offsets[-1]
+        rows = perm.dest_row[kept]
+        assert sorted(rows.tolist()) == list(range(R))          # bijection onto [0, R)
+        assert np.all(perm.dest_row[~kept] == -1)
+        for t, k in zip(*np.nonzero(kept)):
+            row = perm.dest_row[t, k]
+            assert perm.row_token[row] == t
+            e = idx[t, k]
+            assert perm.offsets[e] <= row < perm.offsets[e + 1]
+        for e in range(N):                                       # ascending token order
+            seg = perm.row_token[perm.offsets[e]:perm.offsets[e + 1]]
+            assert np.all(np.diff(seg) > 0)
+        # the kept routes of each expert are exactly its earliest requesting tokens
+        for e in range(N):
+            toks = [t for t in range(T) if e in idx[t]]
+            keep_n = len(toks) if cap < 0 else min(cap, len(toks))
+            assert perm.row_token[perm.offsets[e]:perm.offsets[e + 1]].tolist() == toks[:keep_n]
+
+
+# --------------------------------------------------------------------------------------
+# a5-a8 experts, shared MLP and combine
+# --------------------------------------------------------------------------------------
+def test_swiglu_against_scalar_loops():
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((3, 5))
+    wg, wu = rng.standard_normal((4, 5)), rng.standard_normal((4, 5))
+    wd = rng.standard_normal((5, 4))
+    H, F = O.swiglu(X, wg, wu, wd)
+    for m in range(3):
+        h = []
+        for j in range(4):
+            a = math.fsum(X[m, k] * wg[j, k] for k in range(5))
+            u = math.fsum(X[m, k] * wu[j, k] for k in range(5))
+            h.append(a / (1 + math.exp(-a)) * u)
+        assert np.allclose(H[m], h, atol=1e-12)
+        f = [math.fsum(h[j] * wd[c, j] for j in range(4)) for c in range(5)]
+        assert np.allclose(F[m], f, atol=1e-12)
+
+
+@pytest.mark.parametrize("cap", [-1, 40])
+def test_dense_decomposition_with_tied_router(cap):
+    """p1 Eq. 81: with every logit tied, S = {0..K-1}, p = 1/K, so the Olmo rule gives
+    r_i = 1 and s = 1; the layer must equal one dense SwiGLU MLP of width K d_r + d_s
+    built by concatenating the selected experts and the shared MLP (p4 Eq. 75). With a
+    capacity, exactly the first `cap` tokens keep their routes."""
+    K, N, T = 3, 6, 64
+    x, wr, experts, sh = small_layer(seed=10, T=T, N=N, K=K, zero_router=True)
+    spec = O.LayerSpec(N=N, K=K, score=O.SOFTMAX, renorm=True, alpha=float(K), s=1.0,
+                       capacity=cap)
+    res = O.forward(spec, x, wr, lambda i: experts[i], sh)
+    assert res.idx.tolist() == [[0, 1, 2]] * T
+    assert np.allclose(res.r, 1.0, atol=1e-15)
+    wg = np.concatenate([experts[i][0] for i in range(K)] + [sh[0][0]])
+    wu = np.concatenate([experts[i][1] for i in range(K)] + [sh[0][1]])
+    wd = np.concatenate([experts[i][2] for i in range(K)] + [sh[0][2]], axis=1)
+    dense = dense_swiglu(x, wg, wu, wd)
+    n_keep = T if cap < 0 else cap
+    assert np.max(np.abs(res.y[:n_keep] - dense[:n_keep])) <= 1e-12 * np.max(np.abs(dense))
+    if cap >= 0:
+        shared_only = dense_swiglu(x, sh[0][0], sh[0][1], sh[0][2])
+        assert np.max(np.abs(res.y[n_keep:] - shared_only[n_keep:])) <= 1e-12
+    assert 3 * 24 + 16 == wg.shape[0]                  # d_act = K d_r + d_s (Eq. 81)
+
+
+def test_shared_collapse_eq76():
+    """p4 Eq. 75-76: several ungated shared experts equal one MLP with concatenated
+    gate/up columns and stacked down rows."""
+    x, _, _, sh = small_layer(seed=11, shared=(10, 8, 6))
+    g = O.shared_output(x, sh)
+    wg = np.concatenate([s[0] for s in sh])
+    wu = np.concatenate([s[1] for s in sh])
+    wd = np.concatenate([s[2] for s in sh], axis=1)
+    assert np.max(np.abs(g - dense_swiglu(x, wg, wu, wd))) <= 1e-12 * np.max(np.abs(g))
+
+
+def test_fig68_toy_collapse_in_float32():
+    """p4 Figure 68: d = 6, widths 10/8/6 (m_s = 24, 3 d m_s = 432 parameters); in float32
+    the partitioned and wide forms differ only by rounding (the page reports 3.0e-8)."""
+    rng = np.random.default_rng(12)
+    d, widths = 6, (10, 8, 6)
+    x = rng.standard_normal((2, d)).astype(np.float32)
+    sh = [(rng.standard_normal((m, d)).astype(np.float32),
+           rng.standard_normal((m, d)).astype(np.float32),
+           rng.standard_normal((d, m)).astype(np.float32)) for m in widths]
+    assert 3 * d * sum(widths) == 432
+
+    def mlp32(x, wg, wu, wd):
+        a = x @ wg.T
+        return ((a / (np.float32(1) + np.exp(-a))) * (x @ wu.T)) @ wd.T
+
+    parts = sum(mlp32(x, *s) for s in sh)
+    wide = mlp32(x, np.concatenate([s[0] for s in sh]), np.concatenate([s[1] for s in sh]),
+                 np.concatenate([s[2] for s in sh], axis=1))
+    assert parts.dtype == np.float32
+    assert np.max(np.abs(parts - wide)) < 1e-5 * max(1.0, float(np.max(np.abs(wide))))
+    g64 = O.shared_output(x.astype(np.float64), [tuple(w.astype(np.float64) for w in s) for s in sh])
+    assert np.max(np.abs(g64 - wide)) < 1e-4 * max(1.0, float(np.max(np.abs(wide))))
+
+
+def test_combine_masks_dropped_routes_and_applies_gate():
+    F = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    dest = np.array([[0, 2], [-1, 1], [-1, -1]])
+    r = np.array([[0.5, 2.0], [9.0, 1.0], [7.0, 7.0]])
+    G = np.array([[1.0, 1.0], [2.0, 2.0], [3.0, 3.0]])
+    s = np.array([0.1, 0.2, 0.3])
+    y = O.combine(F, dest, r, G, s)
+    assert np.allclose(y, [[0.5 + 10 + 0.1, 1 + 12 + 0.1], [3 + 0.4, 4 + 0.4], [0.9, 0.9]])
+    assert np.allclose(O.combine(F, dest, r, None), [[10.5, 13.0], [3.0, 4.0], [0.0, 0.0]])
+
+
+def test_forward_tokens_matches_whole_layer():
+    x, wr, experts, sh = small_layer(seed=13, T=50, N=8, K=3)
+    spec = O.LayerSpec(N=8, K=3, alpha=3.0, capacity=12)
+    res = O.forward(spec, x, wr, lambda i: experts[i], sh)
+    toks = [0, 7, 21, 49]
+    y = O.forward_tokens(spec, toks, x, res.idx, res.r, res.perm.dest_row,
+                         lambda i: experts[i], sh)
+    assert np.max(np.abs(y - res.y[toks])) < 1e-12
+
+
+def test_forward_scale_matches_eq85():
+    """p1 Section 21.3: at random init the MoE/dense mean-square output ratio follows
+    Eq. 85 (statistical check, +-6%), and the Table 37 conventions reproduce the four
+    Figure 70(a) RMS ratios from E[sum p^2] = 0.2589."""
+    g = golden("fig70_forward_scale.json")
+    d_r, d_s, K = g["d_r"], g["d_s"], g["K"]
+    d_act = K * d_r + d_s
+    conv = {"olmo": (K, 1.0), "routed_unit_sum": (1.0, 1.0), "equal_branch_mass": (0.5, 0.5),
+            "width_proportional": (K * d_r / d_act, d_s / d_act)}
+    sp2 = g["E_sum_p2"]
+    for name, (a, s) in conv.items():
+        ratio = (d_r * a * a * sp2 + d_s * s * s) / d_act          # Eq. 85 with sum r^2 = a^2 sum p^2
+        assert math.sqrt(ratio) == pytest.approx(g["rms_ratio"][name], abs=1.5e-3), name
+    assert (d_r * K * K * sp2 + d_s) / d_act == pytest.approx(g["predicted_variance_ratio_olmo"], abs=1e-3)
+
+    # statistical check on a scaled-down layer (d_model = d_r = 256, d_s = 128, N = 48, K = 4)
+    rng = np.random.default_rng(14)
+    T, d, dr, ds, N = 512, 256, 256, 128, 48
+    std = 1.0 / math.sqrt(d)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) * 0.02
+    experts = [(rng.standard_normal((dr, d)) * std, rng.standard_normal((dr, d)) * std,
+                rng.standard_normal((d, dr)) * std) for _ in range(N)]
+    sh = [(rng.standard_normal((ds, d)) * std, rng.standard_normal((ds, d)) * std,
+           rng.standard_normal((d, ds)) * std)]
+    spec = O.LayerSpec(N=N, K=K, alpha=float(K), s=1.0)
+    res = O.forward(spec, x, wr, lambda i: experts[i], sh)
+    dense = np.zeros_like(res.y)
+    pred = 0.0
+    for t in range(T):
+        dense[t] = sum(dense_swiglu(x[t:t + 1], *experts[i])[0] for i in res.idx[t]) + \
+            dense_swiglu(x[t:t + 1], *sh[0])[0]
+        pred += eq85_ratio(dr, ds, res.r[t].tolist(), 1.0)
+    measured = np.sum(res.y ** 2) / np.sum(dense ** 2)
+    assert measured == pytest.approx(pred / T, rel=0.06)
+    # branch scale follows intermediate width: RMS(g) / RMS(f_i) ~ sqrt(d_s / d_r)
+    shared_rms = np.sqrt(np.mean(res.G ** 2))
+    routed_rms = np.sqrt(np.mean(res.F_perm ** 2))
+    assert shared_rms / routed_rms == pytest.approx(math.sqrt(ds / dr), rel=0.05)
+
+
+# --------------------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin above fail
+# --------------------------------------------------------------------------------------
+def _swiglu_transposed_gate(X, wg, wu, wd):
+    X = np.asarray(X, np.float64)
+    H = O.silu(X @ np.asarray(wu, np.float64).T) * (X @ np.asarray(wg, np.float64).T)
+    return H, H @ np.asarray(wd, np.float64).T
+
+
+def _combine_without_shared(F, dest, r, G=None, s=1.0):
+    return _orig_combine(F, dest, r, None, s)
+
+
+def _topk_high_index_ties(keys, K):
+    keys = np.asarray(keys)
+    T, N = keys.shape
+    order = np.lexsort((-np.arange(N)[None, :].repeat(T, 0), -keys), axis=-1)
+    return order[:, :K].astype(np.int32)
+
+
+def _keep_last_come(idx, N, capacity):
+    kept = _orig_keep(idx[::-1], N, capacity)
+    return kept[::-1]
+
+
+def _coeff_without_alpha(z, idx, score, renorm, alpha):
+    return _orig_coeff(z, idx, score, renorm, 1.0)
+
+
+_orig_combine = O.combine
+_orig_keep = O.keep_routes
+_orig_coeff = O.route_coefficients
+
+MUTATIONS = {
+    "gate/up swapped": ("swiglu", _swiglu_transposed_gate,
+                        [test_swiglu_against_scalar_loops, test_dense_decomposition_with_tied_router]),
+    "shared term dropped": ("combine", _combine_without_shared,
+                            [test_combine_masks_dropped_routes_and_applies_gate,
+                             test_dense_decomposition_with_tied_router]),
+    "ties to high index": ("topk_select", _topk_high_index_ties,
+                           [test_topk_brute_force_with_forced_ties,
+                            test_topk_all_equal_and_k_equals_n]),
+    "last come kept": ("keep_routes", _keep_last_come,
+                       [test_fig41_per_expert_capacity,
+                        test_keep_closed_form_and_permutation_invariants]),
+    "alpha ignored": ("route_coefficients", _coeff_without_alpha,
+                      [test_fig69_olmo_rule_worked_example, test_coefficient_sums_per_mode]),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad, pins = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, bad)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            if pin is test_dense_decomposition_with_tied_router:
+                pin(-1)
+            else:
+                pin()
