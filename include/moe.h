@@ -1,0 +1,244 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) forward pass of one mixture-of-experts layer.
+ *
+ * The layer, in the notation of the source pages:
+ *   router   z = x W_r^T (+ b), scores, top-K selection S(x), routed coefficients r_i
+ *            ("Section 21: Merging Routed and Shared Expert Activations", Eq. 80 and 83;
+ *             "Appendix E: Expert-Merge Normalization in Public MoE Models", Table 52)
+ *   capacity requested counts C^req, kept counts C^keep = M_i, offsets o_i
+ *            ("Section 10: Routing, Capacity, and Load Balancing", Eq. 19, 21, 25, 26)
+ *   experts  E(x) = [SiLU(x W_g) * (x W_u)] W_d, run as a grouped GEMM over the packed
+ *            per-expert segments ("Section 20: One Shared Expert Is All You Need", Eq. 74)
+ *   combine  y = sum_{i in S(x)} r_i f_i(x) + s(x) g(x)   (Section 21, Eq. 80)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise. The caller owns every buffer;
+ *     the library allocates and frees nothing, keeps no state between calls and is
+ *     re-entrant. Scratch memory comes from a caller-provided workspace whose size is
+ *     returned by the matching *_workspace_size() query.
+ *   - Every call only enqueues kernels on `stream` and returns without synchronizing.
+ *     Results are valid once the stream has completed.
+ *   - Matrices are row-major. Weights use the layout of a PyTorch Linear weight, i.e.
+ *     they are stored transposed with respect to the pages' row-vector notation, so the
+ *     reduction dimension is contiguous: w_gate[i] = W_g,i^T with shape [d_ff][d_model],
+ *     w_up[i] = W_u,i^T [d_ff][d_model], w_down[i] = W_d,i^T [d_model][d_ff],
+ *     w_router = W_r^T [N][d_model].
+ *   - dtype MOE_BF16: x, weights, packed rows, expert outputs and y are bfloat16 (uint16
+ *     bit patterns); logits, coefficients, gates and every accumulator are float32.
+ *     dtype MOE_F32: everything is float32.
+ *   - Return value: MOE_OK, or a negative moe_status. Arguments are validated before any
+ *     kernel is enqueued; on error nothing is enqueued. MOE_ERR_HIP reports a failed
+ *     launch; faults inside a kernel surface when the stream is synchronized.
+ *   - Limits: 1 <= K <= min(N, 16), N <= 256, d_model and d_ff multiples of 64.
+ *     Inputs must be finite. Inputs and outputs must not alias.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, K > N, bad enum, short buffer */
+  MOE_ERR_UNSUPPORTED = -2, /* outside the limits listed above */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_size() query */
+  MOE_ERR_HIP = -4          /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Router score functions (Appendix E, Table 52):
+ *  SOFTMAX           q = softmax over all N logits; renorm: r_i = alpha q_i / sum_S q_j
+ *                    (Olmo rule with alpha = K, Section 21 Eq. 83), else r_i = alpha q_i
+ *                    (routed mass m_K(x) < 1, Qwen1.5/2 and OLMoE rows)
+ *  SIGMOID           sigmoid affinities; renorm: r_i = alpha sigma_i / sum_S sigma_j
+ *                    (DeepSeek-V3 row, alpha = 2.5), else r_i = alpha sigma_i
+ *  SOFTMAX_SELECTED  softmax over the K selected logits, times alpha (Mixtral row)
+ * Selection always ranks the float32 logit z (+ b): every score is monotone in it.
+ * Ties go to the lower expert index; -0.0 ties +0.0. The K slots of a token are ordered
+ * by descending logit, ties by ascending index. */
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0,
+  MOE_SCORE_SIGMOID = 1,
+  MOE_SCORE_SOFTMAX_SELECTED = 2
+} moe_score;
+
+/* Host. Short static description of a status code. */
+const char* moe_status_string(int status);
+
+/* Host. Per-expert capacity ceil(c * K * T / N): the independent per-expert limit of
+ * Section 10 Eq. 25 with T_route = K T routes and N_local = N experts on one GPU,
+ * evaluated in double precision. Returns -1 when c < 0 (unlimited capacity). */
+int moe_capacity_from_factor(double c, int K, int T, int N);
+
+/* Host. Rows needed for packed per-expert buffers: min(K T, N capacity), or K T when
+ * capacity < 0. Every kept route owns one row (Section 10 Eq. 26). */
+int moe_max_rows(int T, int N, int K, int capacity);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route: router logits, scores, top-K selection and routed coefficients, plus the
+ * requested counts C_i^req = #{t : i in S_t} (Section 10 Eq. 19).
+ *
+ *   T, d_model, N, K   tokens, model width, routed experts, experts selected per token
+ *   score, renorm      score function (moe_score) and selected renormalization (0/1);
+ *                      renorm is ignored for SOFTMAX_SELECTED
+ *   alpha              routed scale: r_i = alpha p_i (Appendix E)
+ *   dt                 moe_dtype of x and w_router
+ *   x                  [T][d_model]
+ *   w_router           [N][d_model]
+ *   logit_bias         [N] float32 added to every logit, or NULL
+ *   w_shared_gate      [d_model] (dtype dt) learned shared-gate vector w_s, or NULL;
+ *                      when given, s_tok[t] = sigmoid(x_t . w_s) (Table 52, Qwen rows)
+ *   logits             [T][N] float32: logits_mode 0 -> output (z + b), may be NULL;
+ *                      logits_mode 1 -> input, and x, w_router, logit_bias and
+ *                      w_shared_gate are ignored (s_tok must then be NULL)
+ *   topk_idx           [T][K] int32 out: selected experts
+ *   topk_r             [T][K] float32 out: routed coefficients r
+ *   s_tok              [T] float32 out, or NULL (required iff w_shared_gate != NULL)
+ *   C_req              [N] int32 out, or NULL
+ *   workspace          moe_route_workspace_size(T, N, K) bytes (may be NULL if 0)
+ * ------------------------------------------------------------------------------- */
+size_t moe_route_workspace_size(int T, int N, int K);
+int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
+              const void* x, const void* w_router, const float* logit_bias,
+              const void* w_shared_gate, float* logits, int logits_mode, int32_t* topk_idx,
+              float* topk_r, float* s_tok, int32_t* C_req, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_permute: requested counts, per-expert capacity admission, offsets, restoration
+ * map and the packed rows (Section 10 Eq. 19, 21, 25, 26 and Section 10.3).
+ *
+ *   capacity           routes kept per expert (first come by token index), < 0 = all
+ *   x                  [T][d_model] (dtype dt)
+ *   topk_idx           [T][K] int32 in (each row holds K distinct experts in [0, N))
+ *   C_req, C_keep      [N] int32 out: requested and kept counts (M_i = C_keep[i])
+ *   offsets            [N+1] int32 out: o_0 = 0, o_{i+1} = o_i + M_i
+ *   dest_row           [T][K] int32 out: packed row of each route, -1 when dropped
+ *   row_token          [max_rows] int32 out: source token of packed rows [0, o_N)
+ *   x_perm             [max_rows][d_model] out: x_perm[dest_row[t][k]] = x[t]; expert i
+ *                      owns rows [o_i, o_{i+1}), rows in ascending token order; rows at
+ *                      and beyond o_N are left untouched
+ *   max_rows           >= moe_max_rows(T, N, K, capacity)
+ *   workspace          moe_permute_workspace_size(T, N, K) bytes
+ * ------------------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int T, int N, int K);
+int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const void* x,
+                const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep, int32_t* offsets,
+                int32_t* dest_row, int32_t* row_token, void* x_perm, int max_rows,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_grouped_swiglu: G SwiGLU experts over densely packed row segments, as a grouped
+ * GEMM over the real counts (no padding rows):
+ *   for each group g, rows r in [offsets[g], offsets[g+1]):
+ *     h[r]   = SiLU(a[r] W_g,g) * (a[r] W_u,g)        [d_ff]     (Section 20 Eq. 74)
+ *     out[r] = h[r] W_d,g                              [d_model]
+ *
+ *   G                  groups (routed experts; 1 for the shared MLP)
+ *   a                  [max_rows][d_model] input rows
+ *   offsets            [G+1] int32 DEVICE array, non-decreasing, offsets[G] <= max_rows;
+ *                      or NULL for one group covering rows [0, max_rows)
+ *   w_gate, w_up       [G][d_ff][d_model]
+ *   w_down             [G][d_model][d_ff]
+ *   h                  [max_rows][d_ff] out (intermediate activation)
+ *   out                [max_rows][d_model] out
+ * Rows outside [offsets[0], offsets[G]) are neither read nor written.
+ * Several ungated shared experts are run as ONE group whose weights are the
+ * concatenation of the gate/up rows and of the down columns (Section 20 Eq. 75-76).
+ * ------------------------------------------------------------------------------- */
+int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, const void* a,
+                       const int32_t* offsets, int max_rows, const void* w_gate,
+                       const void* w_up, const void* w_down, void* h, void* out,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_grouped_gemm: ONE pass of the grouped SwiGLU expert, the building block that
+ * moe_grouped_swiglu runs twice:
+ *   swiglu = 1: out[r] = SiLU(a[r] W0_g^T) * (a[r] W1_g^T)   (w0 = w_gate, w1 = w_up,
+ *               each [G][N_dim][K_dim]; out = h, [max_rows][N_dim])
+ *   swiglu = 0: out[r] = a[r] W0_g^T                          (w0 = w_down [G][N_dim][K_dim],
+ *               w1 unused)
+ * for rows r of group g in [offsets[g], offsets[g+1]) (Section 20 Eq. 74 over the
+ * real-count offsets of Section 10 Eq. 26). K_dim and N_dim are multiples of 64;
+ * offsets as in moe_grouped_swiglu.
+ * ------------------------------------------------------------------------------- */
+int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, const void* a,
+                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                     void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine: y[t] = sum_{k : dest_row[t][k] >= 0} r[t][k] f_perm[dest_row[t][k]]
+ *                     + s_t g[t]                                   (Section 21 Eq. 80)
+ * Dropped routes contribute nothing and the kept coefficients are not renormalized
+ * (Section 10.3). Accumulation is float32 in slot order k = 0..K-1, then the shared
+ * term.
+ *
+ *   f_perm             [rows][d_model] packed expert outputs
+ *   dest_row, topk_r   [T][K]
+ *   g                  [T][d_model] shared-expert output, or NULL (no shared expert)
+ *   s                  shared gain, used when s_tok == NULL
+ *   s_tok              [T] float32 per-token shared gate, or NULL
+ *   y                  [T][d_model] out
+ * ------------------------------------------------------------------------------- */
+int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
+                const int32_t* dest_row, const float* topk_r, const void* g, float s,
+                const float* s_tok, void* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_forward: the whole layer: route -> permute -> grouped SwiGLU experts -> shared
+ * MLP -> combine, all enqueued on `stream` with no host synchronization (counts and
+ * offsets stay on the device).
+ * ------------------------------------------------------------------------------- */
+typedef struct moe_forward_args {
+  int T, d_model, N, K;
+  int d_r;               /* routed expert width */
+  int d_s;               /* shared MLP width (sum of the ungated shared widths), 0 = none */
+  int score, renorm;     /* moe_score, 0/1 */
+  float alpha;           /* routed scale */
+  float s;               /* shared gain when w_shared_gate == NULL */
+  int capacity;          /* routes kept per expert, < 0 = unlimited */
+  int dt;                /* moe_dtype */
+  const void* x;         /* [T][d_model] */
+  const void* w_router;  /* [N][d_model] */
+  const float* logit_bias;    /* [N] or NULL */
+  const void* w_shared_gate;  /* [d_model] or NULL */
+  const void* w_gate;    /* [N][d_r][d_model] */
+  const void* w_up;      /* [N][d_r][d_model] */
+  const void* w_down;    /* [N][d_model][d_r] */
+  const void* ws_gate;   /* [d_s][d_model] (NULL when d_s == 0) */
+  const void* ws_up;     /* [d_s][d_model] */
+  const void* ws_down;   /* [d_model][d_s] */
+  void* y;               /* [T][d_model] out */
+  /* Optional outputs: when non-NULL the intermediate is written there, otherwise it
+   * lives in the workspace. Shapes as in the per-stage entry points; `rows` below is
+   * moe_max_rows(T, N, K, capacity). */
+  float* logits;         /* [T][N] */
+  int32_t* topk_idx;     /* [T][K] */
+  float* topk_r;         /* [T][K] */
+  float* s_tok;          /* [T] */
+  int32_t* C_req;        /* [N] */
+  int32_t* C_keep;       /* [N] */
+  int32_t* offsets;      /* [N+1] */
+  int32_t* dest_row;     /* [T][K] */
+  int32_t* row_token;    /* [rows] */
+  void* x_perm;          /* [rows][d_model] */
+  void* h_perm;          /* [rows][d_r] */
+  void* f_perm;          /* [rows][d_model] */
+  void* g;               /* [T][d_model] shared output */
+} moe_forward_args;
+
+size_t moe_forward_workspace_size(const moe_forward_args* args);
+int moe_forward(const moe_forward_args* args, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

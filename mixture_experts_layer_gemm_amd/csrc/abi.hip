@@ -1,0 +1,291 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and the
+// per-stage launch sequence. Declarations and the contract of every entry point are in
+// include/moe.h. Nothing here allocates device memory or synchronizes the stream.
+#include <climits>
+#include <cmath>
+#include <cstddef>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+int nchunks_of(int T) { return (T + moe::kChunk - 1) / moe::kChunk; }
+
+int check_router_dims(int T, int d_model, int N, int K) {
+  if (T < 0 || d_model <= 0 || N <= 0 || K <= 0 || K > N) return MOE_ERR_INVALID_ARG;
+  if (K > moe::kMaxK || N > moe::kMaxN || d_model % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_dtype(int dt) { return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_INVALID_ARG; }
+
+size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+#define MOE_TRY(expr)                        \
+  do {                                       \
+    const int st_ = (expr);                  \
+    if (st_ != MOE_OK) return st_;           \
+  } while (0)
+#define MOE_HIP(expr)                                  \
+  do {                                                 \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;      \
+  } while (0)
+
+// Workspace layout shared by moe_route and moe_permute: chunk histograms and
+// in-chunk ranks, then (route only) scratch for C_keep/offsets.
+struct CountWs {
+  int32_t* hist;
+  int32_t* loc_rank;
+  int32_t* c_keep;
+  int32_t* offsets;
+};
+
+size_t carve_count(void* ws, int T, int N, int K, bool with_scan_scratch, CountWs* out) {
+  Carver c(ws);
+  CountWs w;
+  w.hist = c.take<int32_t>(static_cast<size_t>(nchunks_of(T)) * N);
+  w.loc_rank = c.take<int32_t>(static_cast<size_t>(T) * K);
+  w.c_keep = with_scan_scratch ? c.take<int32_t>(N) : nullptr;
+  w.offsets = with_scan_scratch ? c.take<int32_t>(N + 1) : nullptr;
+  if (out) *out = w;
+  return c.off;
+}
+
+struct FwdWs {
+  float* topk_r;
+  int32_t* topk_idx;
+  float* s_tok;
+  int32_t *hist, *loc_rank, *C_req, *C_keep, *offsets, *dest_row, *row_token;
+  void *x_perm, *h_perm, *f_perm, *g, *h_shared;
+};
+
+size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
+  Carver c(ws);
+  FwdWs w;
+  const size_t T = a->T, K = a->K, N = a->N, d = a->d_model;
+  const size_t rows = static_cast<size_t>(moe_max_rows(a->T, a->N, a->K, a->capacity));
+  const size_t es = esize(a->dt);
+  const bool gate = a->w_shared_gate != nullptr;
+  w.topk_idx = a->topk_idx ? a->topk_idx : c.take<int32_t>(T * K);
+  w.topk_r = a->topk_r ? a->topk_r : c.take<float>(T * K);
+  w.s_tok = !gate ? nullptr : (a->s_tok ? a->s_tok : c.take<float>(T));
+  w.hist = c.take<int32_t>(static_cast<size_t>(nchunks_of(a->T)) * N);
+  w.loc_rank = c.take<int32_t>(T * K);
+  w.C_req = a->C_req ? a->C_req : c.take<int32_t>(N);
+  w.C_keep = a->C_keep ? a->C_keep : c.take<int32_t>(N);
+  w.offsets = a->offsets ? a->offsets : c.take<int32_t>(N + 1);
+  w.dest_row = a->dest_row ? a->dest_row : c.take<int32_t>(T * K);
+  w.row_token = a->row_token ? a->row_token : c.take<int32_t>(rows);
+  w.x_perm = a->x_perm ? a->x_perm : static_cast<void*>(c.take<char>(rows * d * es));
+  w.h_perm = a->h_perm ? a->h_perm : static_cast<void*>(c.take<char>(rows * a->d_r * es));
+  w.f_perm = a->f_perm ? a->f_perm : static_cast<void*>(c.take<char>(rows * d * es));
+  if (a->d_s > 0) {
+    w.g = a->g ? a->g : static_cast<void*>(c.take<char>(T * d * es));
+    w.h_shared = c.take<char>(T * static_cast<size_t>(a->d_s) * es);
+  } else {
+    w.g = nullptr;
+    w.h_shared = nullptr;
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_capacity_from_factor(double c, int K, int T, int N) {
+  if (c < 0.0 || N <= 0) return -1;
+  const double v = std::ceil(c * K * T / N);
+  return v >= static_cast<double>(INT_MAX) ? INT_MAX : static_cast<int>(v);
+}
+
+int moe_max_rows(int T, int N, int K, int capacity) {
+  const long kt = static_cast<long>(K) * (T > 0 ? T : 0);
+  long r = kt;
+  if (capacity >= 0) {
+    const long nc = static_cast<long>(N) * capacity;
+    r = nc < kt ? nc : kt;
+  }
+  return r > INT_MAX ? INT_MAX : static_cast<int>(r);
+}
+
+size_t moe_route_workspace_size(int T, int N, int K) {
+  if (T <= 0 || N <= 0 || K <= 0) return 0;
+  return carve_count(nullptr, T, N, K, true, nullptr);
+}
+
+int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
+              const void* x, const void* w_router, const float* logit_bias,
+              const void* w_shared_gate, float* logits, int logits_mode, int32_t* topk_idx,
+              float* topk_r, float* s_tok, int32_t* C_req, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_router_dims(T, d_model, N, K));
+  MOE_TRY(check_dtype(dt));
+  if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (logits_mode != 0 && logits_mode != 1) return MOE_ERR_INVALID_ARG;
+  if (!topk_idx || !topk_r) return MOE_ERR_INVALID_ARG;
+  if (logits_mode == 0 && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
+  if (logits_mode == 1 && (!logits || s_tok)) return MOE_ERR_INVALID_ARG;
+  if (logits_mode == 0 && ((w_shared_gate != nullptr) != (s_tok != nullptr)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  CountWs w{};
+  if (C_req) {
+    if (!workspace || workspace_bytes < moe_route_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
+    carve_count(workspace, T, N, K, true, &w);
+  }
+  MOE_HIP(launch_route(T, d_model, N, K, score, renorm, alpha, dt, x, w_router, logit_bias,
+                       logits_mode == 0 ? w_shared_gate : nullptr, logits, logits_mode,
+                       topk_idx, topk_r, s_tok, stream));
+  if (C_req) {
+    MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
+    MOE_HIP(launch_scan(T, N, -1, w.hist, C_req, w.c_keep, w.offsets, stream));
+  }
+  return MOE_OK;
+}
+
+size_t moe_permute_workspace_size(int T, int N, int K) {
+  if (T <= 0 || N <= 0 || K <= 0) return 0;
+  return carve_count(nullptr, T, N, K, false, nullptr);
+}
+
+int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const void* x,
+                const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep, int32_t* offsets,
+                int32_t* dest_row, int32_t* row_token, void* x_perm, int max_rows,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE_TRY(check_router_dims(T, d_model, N, K));
+  MOE_TRY(check_dtype(dt));
+  if (!x || !topk_idx || !C_req || !C_keep || !offsets || !dest_row || !row_token || !x_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows < moe_max_rows(T, N, K, capacity)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < moe_permute_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
+  CountWs w{};
+  carve_count(workspace, T, N, K, false, &w);
+  MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
+  MOE_HIP(launch_scan(T, N, capacity, w.hist, C_req, C_keep, offsets, stream));
+  MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
+                         dest_row, row_token, x_perm, stream));
+  return MOE_OK;
+}
+
+int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, const void* a,
+                       const int32_t* offsets, int max_rows, const void* w_gate,
+                       const void* w_up, const void* w_down, void* h, void* out,
+                       hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (G <= 0 || d_model <= 0 || d_ff <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (G > moe::kMaxN || d_model % 64 != 0 || d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
+  if (!a || !w_gate || !w_up || !w_down || !h || !out) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  MOE_HIP(launch_grouped_gemm(true, G, d_model, d_ff, dt, a, offsets, max_rows, w_gate, w_up, h,
+                              stream));
+  MOE_HIP(launch_grouped_gemm(false, G, d_ff, d_model, dt, h, offsets, max_rows, w_down,
+                              nullptr, out, stream));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, const void* a,
+                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                     void* out, hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (G <= 0 || K_dim <= 0 || N_dim <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (swiglu != 0 && swiglu != 1) return MOE_ERR_INVALID_ARG;
+  if (G > moe::kMaxN || K_dim % 64 != 0 || N_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
+  if (!a || !w0 || (swiglu && !w1) || !out) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  MOE_HIP(launch_grouped_gemm(swiglu == 1, G, K_dim, N_dim, dt, a, offsets, max_rows, w0,
+                              swiglu ? w1 : nullptr, out, stream));
+  return MOE_OK;
+}
+
+int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
+                const int32_t* dest_row, const float* topk_r, const void* g, float s,
+                const float* s_tok, void* y, hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (T < 0 || d_model <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (K > moe::kMaxK || d_model % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!f_perm || !dest_row || !topk_r || !y) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  MOE_HIP(launch_combine(T, d_model, K, dt, f_perm, dest_row, topk_r, g, s, s_tok, y, stream));
+  return MOE_OK;
+}
+
+size_t moe_forward_workspace_size(const moe_forward_args* a) {
+  if (!a || a->T <= 0 || a->N <= 0 || a->K <= 0 || a->d_model <= 0) return 0;
+  return carve_forward(a, nullptr, nullptr);
+}
+
+int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_router_dims(a->T, a->d_model, a->N, a->K));
+  MOE_TRY(check_dtype(a->dt));
+  if (a->score < MOE_SCORE_SOFTMAX || a->score > MOE_SCORE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (a->d_r <= 0 || a->d_s < 0) return MOE_ERR_INVALID_ARG;
+  if (a->d_r % 64 != 0 || a->d_s % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!a->x || !a->w_router || !a->w_gate || !a->w_up || !a->w_down || !a->y)
+    return MOE_ERR_INVALID_ARG;
+  if (a->d_s > 0 && (!a->ws_gate || !a->ws_up || !a->ws_down)) return MOE_ERR_INVALID_ARG;
+  if (a->w_shared_gate && a->d_s == 0) return MOE_ERR_INVALID_ARG;
+  if (a->T == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < moe_forward_workspace_size(a)) return MOE_ERR_WORKSPACE;
+  FwdWs w{};
+  carve_forward(a, workspace, &w);
+  const int T = a->T, d = a->d_model, N = a->N, K = a->K;
+  const int rows = moe_max_rows(T, N, K, a->capacity);
+  MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
+                       a->logit_bias, a->w_shared_gate, a->logits, 0, w.topk_idx, w.topk_r,
+                       w.s_tok, stream));
+  MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
+  MOE_HIP(launch_scan(T, N, a->capacity, w.hist, w.C_req, w.C_keep, w.offsets, stream));
+  MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
+                         w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
+  if (rows > 0) {
+    MOE_HIP(launch_grouped_gemm(true, N, d, a->d_r, a->dt, w.x_perm, w.offsets, rows, a->w_gate,
+                                a->w_up, w.h_perm, stream));
+    MOE_HIP(launch_grouped_gemm(false, N, a->d_r, d, a->dt, w.h_perm, w.offsets, rows,
+                                a->w_down, nullptr, w.f_perm, stream));
+  }
+  if (a->d_s > 0) {
+    MOE_HIP(launch_grouped_gemm(true, 1, d, a->d_s, a->dt, a->x, nullptr, T, a->ws_gate,
+                                a->ws_up, w.h_shared, stream));
+    MOE_HIP(launch_grouped_gemm(false, 1, a->d_s, d, a->dt, w.h_shared, nullptr, T,
+                                a->ws_down, nullptr, w.g, stream));
+  }
+  MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
+                         a->y, stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Shared device helpers and kernel-launcher declarations of the MoE layer library.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 16;     // experts selected per token
+constexpr int kMaxN = 256;    // routed experts (router tile kept in LDS)
+constexpr int kChunk = 64;    // tokens per count chunk (one 64-bit mask per expert)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Workload-group id -> logical tile id so that consecutive logical tiles run on the
+// same XCD (the dispatcher hands workgroups to the 8 XCDs round-robin). Tiles that
+// share weight or activation tiles then share that XCD's L2. Returns -1 for a spare
+// workgroup. `grid` must be a multiple of 8 and >= 8 * ceil(total / 8).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = (total + 7) >> 3;
+  const int slot = bid >> 3;
+  if (slot >= per) return -1;
+  const int t = (bid & 7) * per + slot;
+  return t < total ? t : -1;
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------------
+// launchers (enqueue only; return hipError_t of the launch)
+// ---------------------------------------------------------------------------------
+hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
+                        int dt, const void* x, const void* w_router, const float* logit_bias,
+                        const void* w_shared_gate, float* logits, int logits_mode,
+                        int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream);
+
+hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
+                        int32_t* loc_rank, hipStream_t stream);
+
+hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
+                       int32_t* C_keep, int32_t* offsets, hipStream_t stream);
+
+hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* x,
+                          const int32_t* topk_idx, const int32_t* hist_base,
+                          const int32_t* loc_rank, const int32_t* C_keep,
+                          const int32_t* offsets, int32_t* dest_row, int32_t* row_token,
+                          void* x_perm, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(bool swiglu, int G, int K_dim, int N_dim, int dt, const void* a,
+                               const int32_t* offsets, int max_rows, const void* w0,
+                               const void* w1, void* out, hipStream_t stream);
+
+hipError_t launch_combine(int T, int d_model, int K, int dt, const void* f_perm,
+                          const int32_t* dest_row, const float* topk_r, const void* g,
+                          float s, const float* s_tok, void* y, hipStream_t stream);

@@ -1,0 +1,185 @@
+// Requested counts, per-expert capacity admission, offsets and the packed row copy.
+//
+// Follows "Section 10: Routing, Capacity, and Load Balancing": requested counts
+// (Eq. 19), kept counts M_i and drops (Eq. 21), the independent per-expert capacity
+// (Eq. 25) admitting routes first come by token index, and the real-count offsets
+// o_j = sum_{i<=j} M_i of the densely packed expert segments (Eq. 26).
+//
+// Deterministic by construction: no atomic decides a position.
+//   count   one wave per 64-token chunk: each expert's 64-bit token mask is built with
+//           LDS OR (order-free), so a route's rank inside the chunk is a popcount of
+//           the mask below its lane and the chunk histogram is the mask's popcount.
+//   scan    one workgroup: per-expert running sum over chunks (chunk base ranks and
+//           C^req), C^keep = min(C^req, capacity), exclusive scan -> offsets.
+//   scatter one wave per token: rank = chunk base + rank in chunk; kept iff rank <
+//           C^keep; the token's row is read once (16-byte lanes, coalesced) and written
+//           to each kept destination.
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int CNT_WAVES = 4;
+
+__global__ void __launch_bounds__(CNT_WAVES * kWave)
+count_kernel(int T, int N, int K, const int32_t* __restrict__ topk_idx,
+             int32_t* __restrict__ hist, int32_t* __restrict__ loc_rank) {
+  extern __shared__ unsigned long long masks[];  // [CNT_WAVES][N]
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * CNT_WAVES + w;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  unsigned long long* m = masks + static_cast<size_t>(w) * N;
+  for (int e = lane; e < N; e += kWave) m[e] = 0ull;
+  __syncthreads();
+  const int t = chunk * kChunk + lane;
+  const bool valid = chunk < nchunks && t < T;
+  if (valid) {
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[static_cast<size_t>(t) * K + k];
+      atomicOr(&m[e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[static_cast<size_t>(t) * K + k];
+      loc_rank[static_cast<size_t>(t) * K + k] = __popcll(m[e] & below);
+    }
+  }
+  if (chunk < nchunks)
+    for (int e = lane; e < N; e += kWave)
+      hist[static_cast<size_t>(chunk) * N + e] = __popcll(m[e]);
+}
+
+constexpr int SCAN_THREADS = 256;
+
+// Single workgroup. hist[c][e] (chunk counts) is overwritten with the exclusive
+// running sum over chunks, i.e. the rank of chunk c's first route to expert e.
+__global__ void __launch_bounds__(SCAN_THREADS)
+scan_kernel(int nchunks, int N, int capacity, int32_t* __restrict__ hist,
+            int32_t* __restrict__ C_req, int32_t* __restrict__ C_keep,
+            int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[SCAN_THREADS];
+  const int tid = threadIdx.x;
+  const int per = (N + SCAN_THREADS - 1) / SCAN_THREADS;  // experts per thread (<= 4)
+  int keep[kMaxN * 4 / SCAN_THREADS];
+  int local = 0;
+  for (int j = 0; j < per; ++j) {
+    const int e = tid * per + j;
+    int run = 0;
+    if (e < N) {
+      for (int c = 0; c < nchunks; ++c) {
+        const size_t o = static_cast<size_t>(c) * N + e;
+        const int h = hist[o];
+        hist[o] = run;
+        run += h;
+      }
+      C_req[e] = run;
+    }
+    const int kk = (e < N) ? ((capacity < 0 || run < capacity) ? run : capacity) : 0;
+    if (e < N) C_keep[e] = kk;
+    keep[j] = kk;
+    local += kk;
+  }
+  // inclusive Hillis-Steele scan of the per-thread totals
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = part[tid] - local;
+  for (int j = 0; j < per; ++j) {
+    const int e = tid * per + j;
+    if (e < N) offsets[e] = base;
+    base += keep[j];
+  }
+  if (tid == SCAN_THREADS - 1) offsets[N] = part[tid];
+}
+
+constexpr int SC_WAVES = 4;
+
+template <int EB>  // bytes per element
+__global__ void __launch_bounds__(SC_WAVES * kWave)
+scatter_kernel(int T, int d, int N, int K, const void* __restrict__ x,
+               const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ base,
+               const int32_t* __restrict__ loc_rank, const int32_t* __restrict__ C_keep,
+               const int32_t* __restrict__ offsets, int32_t* __restrict__ dest_row,
+               int32_t* __restrict__ row_token, void* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * SC_WAVES + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int dest = -1;
+  if (lane < K) {
+    const size_t tk = static_cast<size_t>(t) * K + lane;
+    const int e = topk_idx[tk];
+    const int rank = base[static_cast<size_t>(t / kChunk) * N + e] + loc_rank[tk];
+    if (rank < C_keep[e]) dest = offsets[e] + rank;
+    dest_row[tk] = dest;
+    if (dest >= 0) row_token[dest] = t;
+  }
+  const int n16 = d * EB / 16;  // 16-byte pieces per row
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(x) +
+                                                    static_cast<size_t>(t) * d * EB);
+  char* dst0 = static_cast<char*>(x_perm);
+  for (int j0 = 0; j0 < n16; j0 += 4 * kWave) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kWave + lane;
+      if (j < n16) v[u] = src[j];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int dk = __shfl(dest, k, kWave);
+      if (dk < 0) continue;
+      u32x4* dst = reinterpret_cast<u32x4*>(dst0 + static_cast<size_t>(dk) * d * EB);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kWave + lane;
+        if (j < n16) dst[j] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
+                        int32_t* loc_rank, hipStream_t stream) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int grid = (nchunks + CNT_WAVES - 1) / CNT_WAVES;
+  const size_t shm = sizeof(unsigned long long) * CNT_WAVES * N;
+  hipLaunchKernelGGL(count_kernel, dim3(grid), dim3(CNT_WAVES * kWave), shm, stream, T, N, K,
+                     topk_idx, hist, loc_rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
+                       int32_t* C_keep, int32_t* offsets, hipStream_t stream) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, nchunks, N, capacity,
+                     hist, C_req, C_keep, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* x,
+                          const int32_t* topk_idx, const int32_t* hist_base,
+                          const int32_t* loc_rank, const int32_t* C_keep,
+                          const int32_t* offsets, int32_t* dest_row, int32_t* row_token,
+                          void* x_perm, hipStream_t stream) {
+  const int grid = (T + SC_WAVES - 1) / SC_WAVES;
+  if (dt == 1)
+    hipLaunchKernelGGL(scatter_kernel<2>, dim3(grid), dim3(SC_WAVES * kWave), 0, stream, T,
+                       d_model, N, K, x, topk_idx, hist_base, loc_rank, C_keep, offsets,
+                       dest_row, row_token, x_perm);
+  else
+    hipLaunchKernelGGL(scatter_kernel<4>, dim3(grid), dim3(SC_WAVES * kWave), 0, stream, T,
+                       d_model, N, K, x, topk_idx, hist_base, loc_rank, C_keep, offsets,
+                       dest_row, row_token, x_perm);
+  return hipGetLastError();
+}

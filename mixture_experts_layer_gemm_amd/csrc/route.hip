@@ -1,0 +1,259 @@
+// Router: logits z = x W_r^T (+ b), scores, top-K selection and routed coefficients.
+//
+// Follows "Section 21: Merging Routed and Shared Expert Activations" (Eq. 80, 83) and
+// "Appendix E: Expert-Merge Normalization in Public MoE Models" (Table 52) for the
+// score rules, and the router projection of "Shared and Fine-Grained Experts" (a
+// bias-free linear layer from d_model to N).
+//
+// One workgroup (4 waves) owns 16 tokens. Phase 1 computes the 16 x N logit tile: for
+// bf16 with v_mfma_f32_16x16x32_bf16, the d_model reduction split round-robin over the
+// waves in 32-wide steps, operands loaded straight from global memory into the MFMA
+// lane layout (x is streamed once; W_r stays in L2), and the four partial tiles summed
+// in LDS in a fixed order. Phase 2 gives each wave 4 tokens: top-K by K rounds of a
+// wave-wide max over packed (ordered float key, inverted expert index) 64-bit values,
+// which yields the lowest index on ties, then the coefficients in the lanes k < K.
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int BT = 16;         // tokens per workgroup
+constexpr int THREADS = 256;   // 4 waves
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord_key(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Butterfly sum: every lane ends with the same, run-to-run deterministic value
+// (each stage adds a + b on one lane and b + a on its partner, which are equal).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// ---- phase 1, bf16: MFMA logits into part[w][BT][ldz] -----------------------------
+template <int NBT>
+__device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                            const uint16_t* __restrict__ wgate, int T, int d, int N, int NB,
+                            int t0, float* part, int ldz) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int row = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const int tok = min(t0 + row, T - 1);
+  const uint16_t* xr = x + static_cast<size_t>(tok) * d + kq;
+  const uint16_t* br[NBT];
+#pragma unroll
+  for (int nb = 0; nb < NBT; ++nb) {
+    const int n = nb * 16 + row;
+    const uint16_t* p = wr;  // padding columns read row 0; their results are dropped
+    if (n < N) p = wr + static_cast<size_t>(n) * d;
+    else if (n == N && wgate != nullptr) p = wgate;
+    br[nb] = p + kq;
+  }
+  floatx4 acc[NBT];
+#pragma unroll
+  for (int nb = 0; nb < NBT; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = d / 32;
+  for (int ks = w; ks < nks; ks += 4) {
+    const int k0 = ks * 32;
+    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr + k0));
+#pragma unroll
+    for (int nb = 0; nb < NBT; ++nb) {
+      if (nb < NB) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(br[nb] + k0));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
+      }
+    }
+  }
+  // D layout of 16x16: lane holds column (lane & 15), rows 4*(lane >> 4) + j.
+  float* pw = part + w * BT * ldz;
+#pragma unroll
+  for (int nb = 0; nb < NBT; ++nb) {
+    if (nb < NB) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pw[((lane >> 4) * 4 + j) * ldz + nb * 16 + row] = acc[nb][j];
+    }
+  }
+}
+
+// ---- phase 1, f32: one wave per (token, column) dot product -----------------------
+__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wr,
+                           const float* __restrict__ wgate, int T, int d, int N, int ncol,
+                           int t0, float* z, int ldz) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int p = w; p < BT * ncol; p += 4) {
+    const int t = p / ncol, n = p % ncol;
+    const int tok = min(t0 + t, T - 1);
+    const float* xr = x + static_cast<size_t>(tok) * d;
+    const float* wrow = (n < N) ? wr + static_cast<size_t>(n) * d : wgate;
+    float acc = 0.f;
+    for (int k = lane; k < d; k += kWave) acc = fmaf(xr[k], wrow[k], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) z[t * ldz + n] = acc;
+  }
+}
+
+template <int NBT>
+__global__ void __launch_bounds__(THREADS)
+route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
+             const void* __restrict__ x, const void* __restrict__ w_router,
+             const float* __restrict__ logit_bias, const void* __restrict__ w_gate_vec,
+             float* __restrict__ logits, int logits_mode, int32_t* __restrict__ topk_idx,
+             float* __restrict__ topk_r, float* __restrict__ s_tok) {
+  constexpr int ldz = NBT * 16 + 1;
+  __shared__ float smem[4 * BT * ldz];  // bf16 path: 4 wave partials; else the tile only
+  float* z = smem;  // final logits tile [BT][ldz]; the bf16 path first uses 4 partials
+  const int t0 = blockIdx.x * BT;
+  const int tid = threadIdx.x;
+  const bool has_gate = (w_gate_vec != nullptr) && logits_mode == 0;
+  const int ncol = N + (has_gate ? 1 : 0);
+
+  if (logits_mode == 1) {
+    for (int i = tid; i < BT * N; i += THREADS) {
+      const int t = i / N, n = i % N;
+      if (t0 + t < T) z[t * ldz + n] = logits[static_cast<size_t>(t0 + t) * N + n];
+    }
+  } else if (dt == 1) {
+    const int NB = (ncol + 15) / 16;
+    logits_bf16<NBT>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                     static_cast<const uint16_t*>(w_gate_vec), T, d, N, NB, t0, smem, ldz);
+    __syncthreads();
+    for (int i = tid; i < BT * ncol; i += THREADS) {
+      const int t = i / ncol, n = i % ncol;
+      const int o = t * ldz + n;
+      const int S = BT * ldz;
+      float v = ((smem[o] + smem[S + o]) + smem[2 * S + o]) + smem[3 * S + o];
+      if (n < N && logit_bias != nullptr) v += logit_bias[n];
+      z[o] = v;
+    }
+  } else {
+    logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
+               static_cast<const float*>(w_gate_vec), T, d, N, ncol, t0, z, ldz);
+    __syncthreads();
+    if (logit_bias != nullptr)
+      for (int i = tid; i < BT * N; i += THREADS) z[(i / N) * ldz + i % N] += logit_bias[i % N];
+  }
+  __syncthreads();
+
+  if (logits_mode == 0 && logits != nullptr) {
+    for (int i = tid; i < BT * N; i += THREADS) {
+      const int t = i / N, n = i % N;
+      if (t0 + t < T) logits[static_cast<size_t>(t0 + t) * N + n] = z[t * ldz + n];
+    }
+  }
+
+  // ---- phase 2: top-K and coefficients, one wave per token --------------------------
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  for (int t = w; t < BT; t += 4) {
+    const int tok = t0 + t;
+    if (tok >= T) break;
+    const float* zr = z + t * ldz;
+    uint64_t cand[kMaxN / kWave];
+#pragma unroll
+    for (int j = 0; j < kMaxN / kWave; ++j) {
+      const int e = lane + j * kWave;
+      cand[j] = (e < N) ? ((static_cast<uint64_t>(ord_key(zr[e])) << 32) |
+                           static_cast<uint64_t>(~static_cast<uint32_t>(e)))
+                        : 0ull;
+    }
+    float selz = 0.f;
+    int sele = 0;
+    for (int k = 0; k < K; ++k) {
+      uint64_t m = cand[0];
+#pragma unroll
+      for (int j = 1; j < kMaxN / kWave; ++j) m = cand[j] > m ? cand[j] : m;
+      m = wave_max_u64(m);
+      const int e = static_cast<int>(~static_cast<uint32_t>(m));
+      if (lane == k) {
+        selz = unord_key(static_cast<uint32_t>(m >> 32));
+        sele = e;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxN / kWave; ++j)
+        if (e == lane + j * kWave) cand[j] = 0ull;
+    }
+    const bool act = lane < K;
+    float r;
+    if (score == 1) {  // sigmoid affinities
+      const float a = act ? sigmoid_f(selz) : 0.f;
+      r = renorm ? alpha * a / wave_sum(a) : alpha * a;
+    } else {
+      const float m = __shfl(selz, 0, kWave);  // top-1 logit = max over all N
+      const float e = act ? expf(selz - m) : 0.f;
+      if (score == 0 && !renorm) {
+        float zsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxN / kWave; ++j) {
+          const int ee = lane + j * kWave;
+          if (ee < N) zsum += expf(zr[ee] - m);
+        }
+        r = alpha * e / wave_sum(zsum);
+      } else {
+        r = alpha * e / wave_sum(e);
+      }
+    }
+    if (act) {
+      topk_idx[static_cast<size_t>(tok) * K + lane] = sele;
+      topk_r[static_cast<size_t>(tok) * K + lane] = r;
+    }
+    if (has_gate && s_tok != nullptr && lane == 0) s_tok[tok] = sigmoid_f(zr[N]);
+  }
+}
+
+template <int NBT>
+hipError_t launch_nbt(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
+                      const void* x, const void* w_router, const float* logit_bias,
+                      const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
+                      float* topk_r, float* s_tok, hipStream_t stream) {
+  const int grid = (T + BT - 1) / BT;
+  hipLaunchKernelGGL(route_kernel<NBT>, dim3(grid), dim3(THREADS), 0, stream, T, d, N, K,
+                     score, renorm, alpha, dt, x, w_router, logit_bias, w_gate_vec, logits,
+                     logits_mode, topk_idx, topk_r, s_tok);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
+                        int dt, const void* x, const void* w_router, const float* logit_bias,
+                        const void* w_shared_gate, float* logits, int logits_mode,
+                        int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream) {
+  const int ncol = N + ((w_shared_gate != nullptr && logits_mode == 0) ? 1 : 0);
+  const int NB = (ncol + 15) / 16;
+#define MOE_ROUTE_CASE(NBT_)                                                                 \
+  if (NB <= NBT_)                                                                            \
+    return launch_nbt<NBT_>(T, d_model, N, K, score, renorm, alpha, dt, x, w_router,        \
+                            logit_bias, w_shared_gate, logits, logits_mode, topk_idx, topk_r, \
+                            s_tok, stream);
+  MOE_ROUTE_CASE(1)
+  MOE_ROUTE_CASE(2)
+  MOE_ROUTE_CASE(4)
+  MOE_ROUTE_CASE(8)
+  MOE_ROUTE_CASE(17)
+#undef MOE_ROUTE_CASE
+  return hipErrorInvalidValue;
+}

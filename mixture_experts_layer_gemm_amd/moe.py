@@ -1,0 +1,281 @@
+"""Thin ctypes binding of the C ABI in include/moe.h.
+
+Argument marshalling only: every stage of the layer runs in the HIP kernels of
+libmoe_mi355x.so. PyTorch supplies device memory (tensors, workspaces) and the stream
+(torch's current stream). Importing this module fails loudly when the library has not
+been built; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, c_double, c_float, c_int, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SOFTMAX_SELECTED = 0, 1, 2
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+class ForwardArgs(ctypes.Structure):
+    """Mirror of moe_forward_args."""
+    _fields_ = [(n, c_int) for n in ("T", "d_model", "N", "K", "d_r", "d_s", "score", "renorm")] + [
+        ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("dt", c_int)] + [
+        (n, c_void_p) for n in ("x", "w_router", "logit_bias", "w_shared_gate", "w_gate", "w_up",
+                                "w_down", "ws_gate", "ws_up", "ws_down", "y", "logits", "topk_idx",
+                                "topk_r", "s_tok", "C_req", "C_keep", "offsets", "dest_row",
+                                "row_token", "x_perm", "h_perm", "f_perm", "g")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library {LIB_PATH} is not built; run "
+                          "`python -m mixture_experts_layer_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    I, F, P, S = c_int, c_float, c_void_p, c_size_t
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [I]),
+        "moe_capacity_from_factor": (I, [c_double, I, I, I]),
+        "moe_max_rows": (I, [I, I, I, I]),
+        "moe_route_workspace_size": (S, [I, I, I]),
+        "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
+        "moe_permute_workspace_size": (S, [I, I, I]),
+        "moe_permute": (I, [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
+        "moe_grouped_swiglu": (I, [I, I, I, I, P, P, I, P, P, P, P, P, P]),
+        "moe_grouped_gemm": (I, [I, I, I, I, I, P, P, I, P, P, P, P]),
+        "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
+        "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
+        "moe_forward": (I, [POINTER(ForwardArgs), P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def declared_symbols(header: str = HEADER) -> list:
+    """Names of the functions declared in include/moe.h."""
+    with open(header) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib.moe_status_string(status).decode()
+
+
+def capacity_from_factor(c: float, K: int, T: int, N: int) -> int:
+    return lib.moe_capacity_from_factor(float(c), K, T, N)
+
+
+def max_rows(T: int, N: int, K: int, capacity: int) -> int:
+    return lib.moe_max_rows(T, N, K, capacity)
+
+
+# ---------------------------------------------------------------------------------------
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn: str, st: int):
+    if st != MOE_OK:
+        raise MoEError(fn, st)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = True,
+              alpha: float = 1.0, logit_bias=None, w_shared_gate=None, logits=None,
+              logits_mode: int = 0, want_logits: bool = False, want_counts: bool = True):
+    """Router stage. Returns dict(topk_idx, topk_r, s_tok, C_req, logits)."""
+    if logits_mode == 1:
+        T, N = logits.shape
+        dev, d, dt = logits.device, 64, MOE_F32
+    else:
+        T, d = x.shape
+        N = w_router.shape[0]
+        dev, dt = x.device, _dt(x)
+        if want_logits and logits is None:
+            logits = torch.empty(T, N, dtype=torch.float32, device=dev)
+    out = dict(topk_idx=torch.empty(T, K, dtype=torch.int32, device=dev),
+               topk_r=torch.empty(T, K, dtype=torch.float32, device=dev),
+               s_tok=(torch.empty(T, dtype=torch.float32, device=dev)
+                      if (w_shared_gate is not None and logits_mode == 0) else None),
+               C_req=torch.empty(N, dtype=torch.int32, device=dev) if want_counts else None,
+               logits=logits)
+    ws = _workspace(lib.moe_route_workspace_size(T, N, K), dev)
+    st = lib.moe_route(T, d, N, K, score, int(renorm), float(alpha), dt,
+                       None if logits_mode == 1 else _ptr(x),
+                       None if logits_mode == 1 else _ptr(w_router),
+                       None if logits_mode == 1 else _ptr(logit_bias),
+                       None if logits_mode == 1 else _ptr(w_shared_gate),
+                       _ptr(logits), logits_mode, _ptr(out["topk_idx"]), _ptr(out["topk_r"]),
+                       _ptr(out["s_tok"]), _ptr(out["C_req"]), _ptr(ws), ws.numel(), _stream())
+    _check("moe_route", st)
+    return out
+
+
+def moe_permute(x, topk_idx, N: int, capacity: int = -1):
+    """Counts, capacity admission, offsets, restoration map and packed rows."""
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    rows = max_rows(T, N, K, capacity)
+    out = dict(C_req=torch.empty(N, dtype=torch.int32, device=dev),
+               C_keep=torch.empty(N, dtype=torch.int32, device=dev),
+               offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
+               dest_row=torch.empty(T, K, dtype=torch.int32, device=dev),
+               row_token=torch.empty(max(rows, 1), dtype=torch.int32, device=dev),
+               x_perm=torch.empty(max(rows, 1), d, dtype=x.dtype, device=dev))
+    ws = _workspace(lib.moe_permute_workspace_size(T, N, K), dev)
+    st = lib.moe_permute(T, d, N, K, capacity, _dt(x), _ptr(x), _ptr(topk_idx),
+                         _ptr(out["C_req"]), _ptr(out["C_keep"]), _ptr(out["offsets"]),
+                         _ptr(out["dest_row"]), _ptr(out["row_token"]), _ptr(out["x_perm"]),
+                         max(rows, 1), _ptr(ws), ws.numel(), _stream())
+    _check("moe_permute", st)
+    return out
+
+
+def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None):
+    """Grouped SwiGLU over packed segments (offsets=None: one group over all rows)."""
+    rows, d = a.shape
+    G, d_ff, _ = w_gate.shape
+    h = torch.empty(rows, d_ff, dtype=a.dtype, device=a.device) if h is None else h
+    out = torch.empty(rows, d, dtype=a.dtype, device=a.device) if out is None else out
+    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), _ptr(a), _ptr(offsets), rows, _ptr(w_gate),
+                                _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out), _stream())
+    _check("moe_grouped_swiglu", st)
+    return h, out
+
+
+def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True):
+    """One grouped GEMM pass: SwiGLU(gate, up) when swiglu, else a plain projection."""
+    rows, Kd = a.shape
+    G, Nd, _ = w0.shape
+    out = torch.empty(rows, Nd, dtype=a.dtype, device=a.device) if out is None else out
+    st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), _ptr(a), _ptr(offsets), rows,
+                              _ptr(w0), _ptr(w1), _ptr(out), _stream())
+    _check("moe_grouped_gemm", st)
+    return out
+
+
+def moe_combine(f_perm, dest_row, topk_r, g=None, s: float = 1.0, s_tok=None, y=None):
+    T, K = dest_row.shape
+    d = f_perm.shape[1]
+    y = torch.empty(T, d, dtype=f_perm.dtype, device=f_perm.device) if y is None else y
+    st = lib.moe_combine(T, d, K, _dt(f_perm), _ptr(f_perm), _ptr(dest_row), _ptr(topk_r),
+                         _ptr(g), float(s), _ptr(s_tok), _ptr(y), _stream())
+    _check("moe_combine", st)
+    return y
+
+
+def pack_shared(shared: Sequence) -> tuple:
+    """Several ungated shared experts -> one MLP: gate/up rows concatenated, down columns
+    concatenated (Section 20, Eq. 75). A weight-layout step, done once at load time."""
+    if not shared:
+        return None
+    if len(shared) == 1:
+        return tuple(w.contiguous() for w in shared[0])
+    return (torch.cat([s[0] for s in shared], 0).contiguous(),
+            torch.cat([s[1] for s in shared], 0).contiguous(),
+            torch.cat([s[2] for s in shared], 1).contiguous())
+
+
+class MoELayer:
+    """Device-resident weights, preallocated outputs and workspace for repeated
+    moe_forward calls on torch's current stream."""
+
+    def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
+                 renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
+                 logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False):
+        self.x = x
+        T, d = x.shape
+        N, d_r, _ = w_gate.shape
+        dev = x.device
+        packed = pack_shared(shared) if shared else None
+        self.tensors = dict(w_router=w_router, w_gate=w_gate, w_up=w_up, w_down=w_down,
+                            logit_bias=logit_bias, w_shared_gate=w_shared_gate)
+        self.packed = packed
+        d_s = packed[0].shape[0] if packed else 0
+        self.y = torch.empty(T, d, dtype=x.dtype, device=dev)
+        self.rows = max_rows(T, N, K, capacity)
+        self.out = {}
+        a = ForwardArgs()
+        a.T, a.d_model, a.N, a.K, a.d_r, a.d_s = T, d, N, K, d_r, d_s
+        a.score, a.renorm, a.alpha, a.s, a.capacity, a.dt = score, int(renorm), alpha, s, capacity, _dt(x)
+        a.x, a.w_router, a.w_gate, a.w_up, a.w_down = (_ptr(x), _ptr(w_router), _ptr(w_gate),
+                                                       _ptr(w_up), _ptr(w_down))
+        a.logit_bias, a.w_shared_gate = _ptr(logit_bias), _ptr(w_shared_gate)
+        if packed:
+            a.ws_gate, a.ws_up, a.ws_down = (_ptr(p) for p in packed)
+        a.y = _ptr(self.y)
+        if keep_intermediates:
+            rows = max(self.rows, 1)
+            i32, f32 = torch.int32, torch.float32
+            spec = dict(logits=((T, N), f32), topk_idx=((T, K), i32), topk_r=((T, K), f32),
+                        C_req=((N,), i32), C_keep=((N,), i32), offsets=((N + 1,), i32),
+                        dest_row=((T, K), i32), row_token=((rows,), i32),
+                        x_perm=((rows, d), x.dtype), h_perm=((rows, d_r), x.dtype),
+                        f_perm=((rows, d), x.dtype))
+            if w_shared_gate is not None:
+                spec["s_tok"] = ((T,), f32)
+            if d_s:
+                spec["g"] = ((T, d), x.dtype)
+            for name, (shape, dtype) in spec.items():
+                t = torch.empty(*shape, dtype=dtype, device=dev)
+                self.out[name] = t
+                setattr(a, name, t.data_ptr())
+        self.args = a
+        self.ws = _workspace(lib.moe_forward_workspace_size(ctypes.byref(a)), dev)
+
+    def forward(self, stream=None):
+        st = lib.moe_forward(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(),
+                             _stream() if stream is None else stream)
+        _check("moe_forward", st)
+        return self.y
+
+
+def moe_forward(x, w_router, w_gate, w_up, w_down, K: int, **kw):
+    """One whole-layer forward. Returns y, or (y, intermediates) with
+    keep_intermediates=True."""
+    keep = kw.pop("keep_intermediates", False)
+    layer = MoELayer(x, w_router, w_gate, w_up, w_down, K, keep_intermediates=keep, **kw)
+    y = layer.forward()
+    return (y, layer.out) if keep else y

@@ -146,11 +146,22 @@ def _draw(cfg: Config, tensor_id: int, index: int, shape, std: float, out=None):
     dtype (uint16 bit patterns for bf16). Writes into `out` when given."""
     v = stream(cfg, tensor_id, index).standard_normal(size=shape, dtype=np.float32)
     v *= np.float32(std)
-    stored = bf16_bits(v) if cfg.dtype == "bf16" else v
-    if out is not None:
-        out[...] = stored
-        return out
-    return stored
+    if cfg.dtype != "bf16":
+        if out is not None:
+            out[...] = v
+            return out
+        return v
+    # round to nearest even in place: u += 0x7FFF + ((u >> 16) & 1); keep the top half
+    u = v.view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u >>= np.uint32(16)
+    if out is None:
+        out = np.empty(shape, dtype=np.uint16)
+    np.copyto(out, u, casting="unsafe")
+    return out
 
 
 def zipf_logit_bias(N: int, a: float = 1.1) -> np.ndarray:

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function that include/moe.h declares, its host helpers agree with the pages' formulas,
+and invalid arguments are rejected with a status code before anything is enqueued."""
+import ctypes
+
+import pytest
+
+from mixture_experts_layer_gemm_amd import moe
+from mixture_experts_layer_gemm_amd import synth
+import oracle.moe_oracle as O
+
+EXPECTED = ["moe_capacity_from_factor", "moe_combine", "moe_forward", "moe_forward_workspace_size",
+            "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_permute", "moe_permute_workspace_size",
+            "moe_route", "moe_route_workspace_size", "moe_status_string"]
+
+
+def test_header_declares_the_expected_entry_points():
+    assert moe.declared_symbols() == EXPECTED
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in moe.declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert moe.status_string(0) == "ok"
+    assert moe.status_string(-3) == "workspace too small"
+    assert moe.status_string(123) == "unknown status"
+
+
+@pytest.mark.parametrize("c,K,T,N", [(1.0, 4, 4096, 64), (1.0, 4, 600, 16), (0.5, 4, 600, 16),
+                                     (1.25, 2, 10, 3), (1.0, 1, 1, 64), (2.0, 8, 8192, 256)])
+def test_capacity_matches_eq25(c, K, T, N):
+    assert moe.capacity_from_factor(c, K, T, N) == O.capacity_from_factor(c, K, T, N)
+
+
+def test_capacity_unlimited_and_max_rows():
+    assert moe.capacity_from_factor(-1.0, 4, 4096, 64) == -1
+    assert moe.max_rows(4096, 64, 4, -1) == 4 * 4096
+    assert moe.max_rows(4096, 64, 4, 256) == 64 * 256
+    assert moe.max_rows(4096, 64, 4, 10) == 640
+    assert moe.max_rows(100, 64, 4, 0) == 0
+
+
+def test_workspace_sizes_are_positive_and_monotone():
+    a = moe.lib.moe_route_workspace_size(4096, 64, 4)
+    b = moe.lib.moe_route_workspace_size(8192, 64, 4)
+    assert 0 < a < b
+    assert moe.lib.moe_permute_workspace_size(0, 64, 4) == 0
+    args = moe.ForwardArgs()
+    args.T, args.d_model, args.N, args.K, args.d_r, args.d_s = 4096, 2048, 64, 4, 2560, 1280
+    args.capacity, args.dt = -1, moe.MOE_BF16
+    ws = moe.lib.moe_forward_workspace_size(ctypes.byref(args))
+    rows = 4 * 4096
+    # x_perm + h_perm + f_perm + g + shared h dominate
+    assert ws >= 2 * (rows * 2048 * 2 + rows * 2560 + 4096 * 2048 + 4096 * 1280)
+
+
+def _route(**kw):
+    a = dict(T=16, d=64, N=8, K=2, score=0, renorm=1, alpha=1.0, dt=1, x=1, w=1, bias=None,
+             gate=None, logits=None, mode=0, idx=1, r=1, s_tok=None, creq=None, ws=None, wsb=0)
+    a.update(kw)
+    return moe.lib.moe_route(a["T"], a["d"], a["N"], a["K"], a["score"], a["renorm"], a["alpha"],
+                             a["dt"], a["x"], a["w"], a["bias"], a["gate"], a["logits"], a["mode"],
+                             a["idx"], a["r"], a["s_tok"], a["creq"], a["ws"], a["wsb"], None)
+
+
+def test_route_rejects_bad_arguments_without_launching():
+    assert _route(K=9) == moe.MOE_ERR_INVALID_ARG            # K > N
+    assert _route(K=0) == moe.MOE_ERR_INVALID_ARG
+    assert _route(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert _route(N=300, K=2) == moe.MOE_ERR_UNSUPPORTED     # router tile limit
+    assert _route(N=32, K=17) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(d=96) == moe.MOE_ERR_UNSUPPORTED            # not a multiple of 64
+    assert _route(dt=7) == moe.MOE_ERR_INVALID_ARG
+    assert _route(score=3) == moe.MOE_ERR_INVALID_ARG
+    assert _route(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert _route(idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert _route(gate=1) == moe.MOE_ERR_INVALID_ARG          # gate needs s_tok
+    assert _route(mode=1) == moe.MOE_ERR_INVALID_ARG          # mode 1 needs logits
+    assert _route(creq=1, ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _route(T=0) == moe.MOE_OK                          # empty input: nothing to do
+
+
+def test_permute_grouped_combine_forward_reject_bad_arguments():
+    L = moe.lib
+    assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 31, 1, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG                               # max_rows < K T
+    assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, None, 0, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert L.moe_permute(0, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, None, 0, None) == moe.MOE_OK
+    assert L.moe_grouped_swiglu(2, 64, 100, 1, 1, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_swiglu(2, 64, 128, 1, 1, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_swiglu(1, 64, 128, 1, 1, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
+    assert L.moe_combine(4, 64, 17, 1, 1, 1, 1, None, 1.0, None, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(4, 64, 2, 1, None, 1, 1, None, 1.0, None, 1, None) == moe.MOE_ERR_INVALID_ARG
+    args = moe.ForwardArgs()
+    args.T, args.d_model, args.N, args.K, args.d_r, args.d_s, args.dt = 16, 64, 8, 2, 64, 0, 1
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG  # NULL x
+    for f in ("x", "w_router", "w_gate", "w_up", "w_down", "y"):
+        setattr(args, f, 1)
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_WORKSPACE
+    args.w_shared_gate = 1                                    # gate without a shared MLP
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    args.w_shared_gate = None
+    args.K = 9
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    args.K, args.T = 2, 0
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_OK
+
+
+def test_synth_streams_are_deterministic_and_bf16_exact():
+    cfg = synth.get_config("S_softmax")
+    a = synth.make_inputs(cfg)
+    b = synth.make_inputs(cfg)
+    assert (a.x == b.x).all() and (a.w_down == b.w_down).all()
+    f = a.as_float(a.x)
+    assert (synth.bf16_bits(f) == a.x).all()          # widening then rounding is exact
+    assert synth.make_inputs(cfg, T=10).x.tolist() == a.x[:10].tolist()
+    bias = synth.zipf_logit_bias(64)
+    assert bias[0] > bias[1] > bias[-1]
