@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
+
+A step is one whole-layer forward (router -> permute -> grouped SwiGLU experts -> shared
+MLP -> combine) over one batch of seeded synthetic tokens resident in HBM. Prints one
+JSON line: whole-layer tokens/s, the grouped-GEMM TFLOP/s, the roofline of the dominant
+kernel (the routed gate/up grouped GEMM with fused SwiGLU), per-stage times and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 64e K=4"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_gemm_amd", "csrc", "gemm_packed.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_olmo64e_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_device(a, dtype, torch):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def gemm_source_sha() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc
+    summary, or None if absent or taken from a different version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != gemm_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_graph(torch, fn, reps: int) -> float:
+    """Average GPU time (ms) of fn() over `reps` calls captured in one HIP graph and
+    replayed, bracketed by events on the replay stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm (not captured)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_eager(torch, fn, reps: int) -> float:
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(inp, sample_tokens: int):
+    """The oracle as it stands, on the first `sample_tokens` tokens of the workload."""
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    c = inp.cfg
+    x = inp.as_float(inp.x[:sample_tokens])
+    cap = -1 if c.capacity_factor is None else O.capacity_from_factor(c.capacity_factor, c.K, sample_tokens, c.N)
+    spec = O.LayerSpec(N=c.N, K=c.K, score=c.score, renorm=c.renorm, alpha=c.alpha, s=c.s, capacity=cap)
+    times = []
+    while len(times) < 3 and sum(times) < 10.0:
+        t0 = time.perf_counter()
+        O.forward(spec, x, inp.as_float(inp.w_router), inp.expert_f32, inp.shared_f32(),
+                  logit_bias=inp.logit_bias,
+                  w_shared_gate=None if inp.w_shared_gate is None else inp.as_float(inp.w_shared_gate))
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample_tokens} of {c.T} tokens of the same layer (all {c.N} experts), fp64 "
+                      f"NumPy forward only, median of {len(times)} runs of {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C1")
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
+              "unsharded on a single MI355X (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_gemm_amd import synth
+    from mixture_experts_layer_gemm_amd import moe
+
+    cfg = synth.get_config(args.workload)
+    log(f"generating {cfg.name} inputs ...")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg)
+    log(f"  {time.time() - t0:.1f} s; uploading")
+    dt = cfg.dtype
+    x = to_device(inp.x, dt, torch)
+    w_router = to_device(inp.w_router, dt, torch)
+    w_gate, w_up, w_down = (to_device(a, dt, torch) for a in (inp.w_gate, inp.w_up, inp.w_down))
+    shared = [tuple(to_device(w, dt, torch) for w in s) for s in inp.shared] or None
+    bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).cuda()
+    gate = None if inp.w_shared_gate is None else to_device(inp.w_shared_gate, dt, torch)
+    T, d, N, K, d_r = cfg.T, cfg.d_model, cfg.N, cfg.K, cfg.d_r
+    cap = moe.capacity_from_factor(cfg.capacity_factor, K, T, N) if cfg.capacity_factor is not None else -1
+    layer = moe.MoELayer(x, w_router, w_gate, w_up, w_down, K, score=cfg.score, renorm=cfg.renorm,
+                         alpha=cfg.alpha, s=cfg.s, capacity=cap, logit_bias=bias, w_shared_gate=gate,
+                         shared=shared, keep_intermediates=True)
+    torch.cuda.synchronize()
+
+    log(f"warmup {args.warmup}, timed {args.steps} steps")
+    for _ in range(args.warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        layer.forward()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = T / (ms / 1e3)
+
+    # ---- per-stage timing on the layer's own buffers ------------------------------
+    o = layer.out
+    R = int(o["offsets"][-1].item())
+    esz = 2 if dt == "bf16" else 4
+    rows = layer.rows
+    h_perm, f_perm = o["h_perm"], o["f_perm"]
+    reps = args.stage_reps
+    log("stage timings")
+    st = {}
+    pk = layer.weights_packed
+    lw = layer.tensors                 # the layer's own (packed) weights
+    st["gemm_gateup_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
+        o["x_perm"], o["offsets"], lw["w_gate"], lw["w_up"], out=h_perm, swiglu=True, packed=pk), reps)
+    st["gemm_down_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
+        h_perm, o["offsets"], lw["w_down"], out=f_perm, swiglu=False, packed=pk), reps)
+    sm = layer.shared_mlp
+    if sm is not None:
+        hs = torch.empty(T, sm[0].shape[0], dtype=x.dtype, device=x.device)
+        g_out = torch.empty(T, d, dtype=x.dtype, device=x.device)
+        st["shared_mlp_ms"] = time_eager(torch, lambda: moe.moe_grouped_swiglu(
+            x, None, sm[0][None], sm[1][None], sm[2][None], h=hs, out=g_out, packed=pk), reps)
+    logits = torch.empty(T, N, dtype=torch.float32, device=x.device)
+    st["route_ms"] = time_graph(torch, lambda: moe.moe_route(
+        x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
+        w_shared_gate=gate, want_counts=False), reps)
+    idx = o["topk_idx"]
+    st["permute_ms"] = time_graph(torch, lambda: moe.moe_permute(x, idx, N, cap), reps)
+    y2 = torch.empty_like(layer.y)
+    st["combine_ms"] = time_graph(torch, lambda: moe.moe_combine(
+        f_perm, o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2), reps)
+
+    flops_gateup = 4.0 * R * d * d_r
+    flops_down = 2.0 * R * d * d_r
+    act_experts = int((o["C_keep"] > 0).sum().item())
+    bytes_gateup = 2 * act_experts * d_r * d * esz + R * d * esz + R * d_r * esz
+    gemm_tflops = (flops_gateup + flops_down) / ((st["gemm_gateup_ms"] + st["gemm_down_ms"]) * 1e-3) / 1e12
+    achieved = flops_gateup / (st["gemm_gateup_ms"] * 1e-3) / 1e12
+    traffic = measured_traffic()
+    hbm = {
+        "route": (T * d * esz + N * d * esz + T * K * 8) / (st["route_ms"] * 1e-3) / 1e9,
+        "permute": (T * d * esz + R * d * esz + T * K * 16) / (st["permute_ms"] * 1e-3) / 1e9,
+        "combine": (R * d * esz + (2 if layer.shared_mlp is not None else 1) * T * d * esz + T * K * 8)
+        / (st["combine_ms"] * 1e-3) / 1e9,
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else "f32",
+        "data": "synthetic: seeded normals (x ~ N(0,1), weights ~ N(0, %g)), bf16-rounded" % cfg.std_w,
+        "config": {"workload": f"{cfg.name}: T={T} d_model={d} N={N} K={K} d_r={d_r} d_s={cfg.d_s}",
+                   "T": T, "d_model": d, "N": N, "K": K, "d_r": d_r, "d_s": cfg.d_s,
+                   "score": ["softmax", "sigmoid", "softmax_selected"][cfg.score],
+                   "renorm": cfg.renorm, "alpha": cfg.alpha, "capacity": cap,
+                   "kept_routes": R, "active_experts": act_experts},
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "routed gate/up grouped GEMM + fused SwiGLU (gemm_packed_kernel<true,true>)"
+                     if pk else "routed gate/up grouped GEMM + fused SwiGLU (gemm_bf16_kernel<true,true>)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": bytes_gateup,
+                     "flops_per_launch": flops_gateup},
+        "stages_ms": {k.replace("_ms", ""): round(v, 4) for k, v in st.items()},
+        "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
+    }
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample_tokens, T))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -149,18 +149,20 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
  *   w_down             [G][d_model][d_ff]
  *   h                  [max_rows][d_ff] out (intermediate activation)
  *   out                [max_rows][d_model] out
+ *   packed             0: weights row-major as above; 1: weights in the packed layout
+ *                      written by moe_pack_weights (bf16 only; the fast path)
  * Rows outside [offsets[0], offsets[G]) are neither read nor written.
  * Several ungated shared experts are run as ONE group whose weights are the
  * concatenation of the gate/up rows and of the down columns (Section 20 Eq. 75-76).
  * ------------------------------------------------------------------------------- */
-int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, const void* a,
+int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
                        const int32_t* offsets, int max_rows, const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_grouped_gemm: ONE pass of the grouped SwiGLU expert, the building block that
- * moe_grouped_swiglu runs twice:
+ * moe_grouped_swiglu runs twice (packed as in moe_grouped_swiglu):
  *   swiglu = 1: out[r] = SiLU(a[r] W0_g^T) * (a[r] W1_g^T)   (w0 = w_gate, w1 = w_up,
  *               each [G][N_dim][K_dim]; out = h, [max_rows][N_dim])
  *   swiglu = 0: out[r] = a[r] W0_g^T                          (w0 = w_down [G][N_dim][K_dim],
@@ -169,9 +171,21 @@ int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, const void* a,
  * real-count offsets of Section 10 Eq. 26). K_dim and N_dim are multiples of 64;
  * offsets as in moe_grouped_swiglu.
  * ------------------------------------------------------------------------------- */
-int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, const void* a,
-                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
-                     void* out, hipStream_t stream);
+int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
+                     const void* a, const int32_t* offsets, int max_rows, const void* w0,
+                     const void* w1, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_pack_weights: one-time re-layout of G row-major bf16 weight matrices
+ * w[G][N_dim][K_dim] into the order in which the bf16 MFMA consumes them:
+ *   w_packed[g][nb][kb][lane][8] = w[g][32 nb + (lane & 31)][16 kb + 8 (lane >> 5) + 0..7]
+ * (nb < N_dim / 32, kb < K_dim / 16, lane < 64). Same size as w; w and w_packed must
+ * not overlap. Gate, up and down weights are each packed as they are passed to the GEMM
+ * (w_gate and w_up with N_dim = d_ff, K_dim = d_model; w_down with N_dim = d_model,
+ * K_dim = d_ff). N_dim and K_dim are multiples of 64. dt must be MOE_BF16.
+ * ------------------------------------------------------------------------------- */
+int moe_pack_weights(int G, int N_dim, int K_dim, int dt, const void* w, void* w_packed,
+                     hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_combine: y[t] = sum_{k : dest_row[t][k] >= 0} r[t][k] f_perm[dest_row[t][k]]
@@ -205,6 +219,8 @@ typedef struct moe_forward_args {
   float s;               /* shared gain when w_shared_gate == NULL */
   int capacity;          /* routes kept per expert, < 0 = unlimited */
   int dt;                /* moe_dtype */
+  int weights_packed;    /* 1: w_gate/w_up/w_down and ws_* are in the moe_pack_weights
+                            layout (bf16; the fast path), 0: row-major */
   const void* x;         /* [T][d_model] */
   const void* w_router;  /* [N][d_model] */
   const float* logit_bias;    /* [N] or NULL */

@@ -197,35 +197,61 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
   return MOE_OK;
 }
 
-int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, const void* a,
+// one grouped GEMM pass on the row-major or the packed-weight kernel
+static hipError_t gemm_pass(bool swiglu, bool packed, int G, int Kd, int Nd, int dt, const void* a,
+                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                     void* out, hipStream_t stream) {
+  if (packed)
+    return launch_grouped_gemm_packed(swiglu, G, Kd, Nd, a, offsets, max_rows, w0, w1, out, stream);
+  return launch_grouped_gemm(swiglu, G, Kd, Nd, dt, a, offsets, max_rows, w0, w1, out, stream);
+}
+
+int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
                        const int32_t* offsets, int max_rows, const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
+  if (packed != 0 && packed != 1) return MOE_ERR_INVALID_ARG;
+  if (packed && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (G <= 0 || d_model <= 0 || d_ff <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
   if (G > moe::kMaxN || d_model % 64 != 0 || d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w_gate || !w_up || !w_down || !h || !out) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(launch_grouped_gemm(true, G, d_model, d_ff, dt, a, offsets, max_rows, w_gate, w_up, h,
-                              stream));
-  MOE_HIP(launch_grouped_gemm(false, G, d_ff, d_model, dt, h, offsets, max_rows, w_down,
-                              nullptr, out, stream));
+  MOE_HIP(gemm_pass(true, packed, G, d_model, d_ff, dt, a, offsets, max_rows, w_gate, w_up, h,
+                    stream));
+  MOE_HIP(gemm_pass(false, packed, G, d_ff, d_model, dt, h, offsets, max_rows, w_down, nullptr,
+                    out, stream));
   return MOE_OK;
 }
 
-int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, const void* a,
-                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
-                     void* out, hipStream_t stream) {
+int moe_pack_weights(int G, int N_dim, int K_dim, int dt, const void* w, void* w_packed,
+                     hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (G <= 0 || N_dim <= 0 || K_dim <= 0 || !w || !w_packed) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16 || N_dim % 64 != 0 || K_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const size_t bytes = static_cast<size_t>(G) * N_dim * K_dim * 2;
+  const char* src = static_cast<const char*>(w);
+  char* dst = static_cast<char*>(w_packed);
+  if (src < dst + bytes && dst < src + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+  MOE_HIP(launch_pack_weights(G, N_dim, K_dim, w, w_packed, stream));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
+                     const void* a, const int32_t* offsets, int max_rows, const void* w0,
+                     const void* w1, void* out, hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
   if (G <= 0 || K_dim <= 0 || N_dim <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
   if (swiglu != 0 && swiglu != 1) return MOE_ERR_INVALID_ARG;
+  if (packed != 0 && packed != 1) return MOE_ERR_INVALID_ARG;
+  if (packed && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (G > moe::kMaxN || K_dim % 64 != 0 || N_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w0 || (swiglu && !w1) || !out) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(launch_grouped_gemm(swiglu == 1, G, K_dim, N_dim, dt, a, offsets, max_rows, w0,
-                              swiglu ? w1 : nullptr, out, stream));
+  MOE_HIP(gemm_pass(swiglu == 1, packed == 1, G, K_dim, N_dim, dt, a, offsets, max_rows, w0,
+                    swiglu ? w1 : nullptr, out, stream));
   return MOE_OK;
 }
 
@@ -258,6 +284,8 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
     return MOE_ERR_INVALID_ARG;
   if (a->d_s > 0 && (!a->ws_gate || !a->ws_up || !a->ws_down)) return MOE_ERR_INVALID_ARG;
   if (a->w_shared_gate && a->d_s == 0) return MOE_ERR_INVALID_ARG;
+  if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_ERR_INVALID_ARG;
+  if (a->weights_packed && a->dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (a->T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_forward_workspace_size(a)) return MOE_ERR_WORKSPACE;
   FwdWs w{};
@@ -271,17 +299,18 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   MOE_HIP(launch_scan(T, N, a->capacity, w.hist, w.C_req, w.C_keep, w.offsets, stream));
   MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
+  const bool pk = a->weights_packed == 1;
   if (rows > 0) {
-    MOE_HIP(launch_grouped_gemm(true, N, d, a->d_r, a->dt, w.x_perm, w.offsets, rows, a->w_gate,
-                                a->w_up, w.h_perm, stream));
-    MOE_HIP(launch_grouped_gemm(false, N, a->d_r, d, a->dt, w.h_perm, w.offsets, rows,
-                                a->w_down, nullptr, w.f_perm, stream));
+    MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, w.x_perm, w.offsets, rows, a->w_gate,
+                      a->w_up, w.h_perm, stream));
+    MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, w.offsets, rows, a->w_down,
+                      nullptr, w.f_perm, stream));
   }
   if (a->d_s > 0) {
-    MOE_HIP(launch_grouped_gemm(true, 1, d, a->d_s, a->dt, a->x, nullptr, T, a->ws_gate,
-                                a->ws_up, w.h_shared, stream));
-    MOE_HIP(launch_grouped_gemm(false, 1, a->d_s, d, a->dt, w.h_shared, nullptr, T,
-                                a->ws_down, nullptr, w.g, stream));
+    MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, nullptr, T, a->ws_gate, a->ws_up,
+                      w.h_shared, stream));
+    MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, nullptr, T, a->ws_down,
+                      nullptr, w.g, stream));
   }
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));

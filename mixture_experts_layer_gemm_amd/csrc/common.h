@@ -32,7 +32,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float silu_f(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -73,6 +75,13 @@ hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* 
 hipError_t launch_grouped_gemm(bool swiglu, int G, int K_dim, int N_dim, int dt, const void* a,
                                const int32_t* offsets, int max_rows, const void* w0,
                                const void* w1, void* out, hipStream_t stream);
+
+hipError_t launch_grouped_gemm_packed(bool swiglu, int G, int K_dim, int N_dim, const void* a,
+                                      const int32_t* offsets, int max_rows, const void* w0p,
+                                      const void* w1p, void* out, hipStream_t stream);
+
+hipError_t launch_pack_weights(int G, int N_dim, int K_dim, const void* w, void* w_packed,
+                               hipStream_t stream);
 
 hipError_t launch_combine(int T, int d_model, int K, int dt, const void* f_perm,
                           const int32_t* dest_row, const float* topk_r, const void* g,

@@ -7,196 +7,160 @@
 //   swiglu = true : h = SiLU(a W_g^T) * (a W_u^T)  (gate and up tiles in one workgroup)
 //   swiglu = false: out = a W^T                     (the down projection)
 //
-// bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * tile = 128 packed rows x 256 weight rows (swiglu: 128 gate + 128 up rows, i.e.
-//     128 output columns; plain: 256 output columns), k-step 32, 4 waves;
-//   * the product is formed transposed (weights as the MFMA A operand, rows as B) so
-//     each lane ends up holding 4 consecutive output columns of one row: 8-byte stores;
-//   * LDS stages are double buffered through registers; 16-byte chunks are XOR
-//     swizzled by row so MFMA operand reads and the staging writes avoid bank conflicts;
-//   * the tile map is rebuilt on the device from the offsets (no host sync): every
-//     workgroup scans the per-group m-tile counts in LDS; the tile order is
-//     (group, m-tile, n-tile) and is laid out XCD-major, so the tiles sharing a weight
-//     slab or an activation slab run together on one XCD and hit its L2.
+// bf16 path (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   * workgroup tile = 128 packed rows x 512 weight rows (swiglu: 256 gate + 256 up
+//     rows = 256 output columns; plain: 512 output columns), 4 waves, one per SIMD,
+//     each wave a 128 x 128 block of 4 x 4 MFMA tiles (256 fp32 accumulators): large
+//     wave tiles keep LDS traffic per MFMA low;
+//   * the k loop streams 32-wide stages through a 3-deep LDS ring filled by
+//     global_load_lds_dwordx4 (gfx950 direct-to-LDS loads, no register staging): each
+//     stage is issued two iterations before it is consumed, so ~80 KB per CU stays in
+//     flight to HBM while the MFMAs run; one barrier per stage;
+//   * 16-byte chunks are XOR-swizzled by row so MFMA operand reads are bank-conflict
+//     free; the DMA lane -> (row, chunk) mapping writes that swizzled layout directly;
+//   * the product is formed transposed (weights are the MFMA A operand, rows the B
+//     operand), so each lane holds 4 consecutive output columns of one row;
+//   * the tile map is rebuilt on the device from the offsets (no host sync); tiles are
+//     ordered (group, n-tile, m-tile) and laid out XCD-major so the m-tiles that share
+//     a weight slab run side by side on one XCD and share its L2.
 // f32 path: a plain LDS-tiled FMA kernel with the same tile map (small fp32 layers).
-#include "common.h"
+#include "gemm_common.h"
 
 using namespace moe;
 
 namespace {
 
-constexpr int BM = 128;                 // packed rows per tile
-constexpr int BNW = 256;                // weight rows per tile
-constexpr int BK = 32;                  // k per stage
 constexpr int THREADS = 256;
-constexpr int A_BYTES = BM * BK * 2;
-constexpr int W_BYTES = BNW * BK * 2;
-constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+constexpr int BM = 128;                    // packed rows per tile
+constexpr int BN = 512;                    // weight rows per tile
+constexpr int BK = 32;                     // k per stage
+constexpr int STAGES = 3;
+constexpr int ROWB = BK * 2;               // bytes per LDS row (4 chunks of 16 B)
+constexpr int X_BYTES = BM * ROWB;         // 8 KB
+constexpr int W_BYTES = BN * ROWB;         // 32 KB
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+constexpr int DMA_BLOCKS = STAGE_BYTES / 1024;      // 1 KB per wave-wide DMA instruction
+constexpr int DMA_PER_WAVE = DMA_BLOCKS / 4;         // 10
+static_assert(DMA_BLOCKS % 4 == 0, "stage must split evenly over 4 waves");
 
-// byte offset of 16-byte chunk kc (0..3) of row r in a [rows][BK] bf16 LDS tile;
-// the XOR pattern spreads 8 (or 16) consecutive rows over distinct banks.
-__device__ __forceinline__ int swz(int r, int kc) {
+// physical 16-byte chunk of logical chunk c (0..3) in LDS row r: bijective per row and
+// spreads 8 (32 banks) or 16 (64 banks) consecutive rows over distinct banks
+__device__ __forceinline__ int swz_chunk(int r, int c) {
   const int f = (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
-  return r * (BK * 2) + ((kc ^ f) << 4);
+  return c ^ f;
 }
-
-struct TileMap {
-  int g, row0, rows, nt;
-};
-
-// Builds the (group, m-tile) prefix in LDS and decodes this workgroup's tile.
-// Returns false for a spare workgroup. All threads must call it.
-__device__ bool decode_tile(const int32_t* __restrict__ offsets, int G, int max_rows, int bm,
-                            int n_tiles, int* s_off, int* s_mstart, TileMap& tm) {
-  const int tid = threadIdx.x;
-  for (int g = tid; g <= G; g += blockDim.x)
-    s_off[g] = (offsets != nullptr) ? offsets[g] : (g == 0 ? 0 : max_rows);
-  __syncthreads();
-  // inclusive scan of m-tile counts (G <= 256 = blockDim)
-  const int cnt = (tid < G) ? ceil_div(s_off[tid + 1] - s_off[tid], bm) : 0;
-  s_mstart[tid + 1] = cnt;
-  if (tid == 0) s_mstart[0] = 0;
-  __syncthreads();
-  for (int off = 1; off < THREADS; off <<= 1) {
-    const int v = (tid >= off) ? s_mstart[tid + 1 - off] : 0;
-    __syncthreads();
-    s_mstart[tid + 1] += v;
-    __syncthreads();
-  }
-  const int total_m = s_mstart[G];
-  const int tile = xcd_remap(blockIdx.x, total_m * n_tiles);
-  if (tile < 0) return false;
-  const int mt = tile / n_tiles;
-  tm.nt = tile - mt * n_tiles;
-  int lo = 0, hi = G - 1;  // largest g with s_mstart[g] <= mt
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_mstart[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  tm.g = lo;
-  tm.row0 = s_off[lo] + (mt - s_mstart[lo]) * bm;
-  tm.rows = min(bm, s_off[lo + 1] - tm.row0);
-  return true;
-}
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_chunk(r, c) << 4); }
 
 // GROUPED = false: one group over rows [0, max_rows) (the shared MLP); a separate
 // instantiation so that profiles tell the routed and the shared launches apart.
 template <bool SWIGLU, bool GROUPED>
-__global__ void __launch_bounds__(THREADS, 2)
+__global__ void __launch_bounds__(THREADS, 1)
 gemm_bf16_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
                  const int32_t* __restrict__ offsets, int max_rows,
                  const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
                  uint16_t* __restrict__ out) {
   __shared__ int s_off[kMaxN + 1];
-  __shared__ int s_mstart[THREADS + 1];
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];
+  __shared__ int s_tstart[THREADS + 1];
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
 
-  constexpr int COLS = SWIGLU ? BNW / 2 : BNW;  // output columns per tile
+  constexpr int COLS = SWIGLU ? BN / 2 : BN;  // output columns per tile
   const int n_tiles = ceil_div(Nd, COLS);
   TileMap tm;
-  if (!decode_tile(GROUPED ? offsets : nullptr, G, max_rows, BM, n_tiles, s_off, s_mstart, tm))
+  if (!decode_tile(GROUPED ? offsets : nullptr, G, max_rows, BM, n_tiles, s_off, s_tstart, tm))
     return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int n0 = tm.nt * COLS;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int n0 = __builtin_amdgcn_readfirstlane(tm.nt * COLS);
   const size_t wstride = static_cast<size_t>(Nd) * Kd;
   const uint16_t* wg = w0 + tm.g * wstride;
   const uint16_t* wu = SWIGLU ? (w1 + tm.g * wstride) : nullptr;
 
-  // staging assignment: A 2 chunks/thread, W 4 chunks/thread
-  const uint16_t* asrc[2];
-  int alds[2];
+  // DMA sources: instruction i of wave w fills 1 KB block b = 4 i + w of a stage;
+  // lane j of it writes 16-byte slot 64 b + j, i.e. (row, physical chunk).
+  const uint16_t* src[DMA_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + i * THREADS;
-    const int r = c >> 2, kc = c & 3;
-    const int src = tm.row0 + min(r, tm.rows - 1);
-    asrc[i] = a + static_cast<size_t>(src) * Kd + kc * 8;
-    alds[i] = swz(r, kc);
-  }
-  const uint16_t* wsrc[4];
-  int wlds[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * THREADS;
-    const int r = c >> 2, kc = c & 3;
-    const uint16_t* base;
-    int n;
-    if (SWIGLU) {
-      base = (r < BNW / 2) ? wg : wu;
-      n = n0 + (r & (BNW / 2 - 1));
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int slot = (4 * i + w) * 64 + lane;
+    if (slot < X_BYTES / 16) {
+      const int r = slot >> 2;
+      const int c = swz_chunk(r, slot & 3);
+      src[i] = a + static_cast<size_t>(tm.row0 + min(r, tm.rows - 1)) * Kd + c * 8;
     } else {
-      base = wg;
-      n = n0 + r;
+      const int ws = slot - X_BYTES / 16;
+      const int r = ws >> 2;
+      const int c = swz_chunk(r, ws & 3);
+      const uint16_t* base;
+      int n;
+      if (SWIGLU) {
+        base = (r < BN / 2) ? wg : wu;
+        n = n0 + (r & (BN / 2 - 1));
+      } else {
+        base = wg;
+        n = n0 + r;
+      }
+      src[i] = base + static_cast<size_t>(min(n, Nd - 1)) * Kd + c * 8;
     }
-    n = min(n, Nd - 1);
-    wsrc[i] = base + static_cast<size_t>(n) * Kd + kc * 8;
-    wlds[i] = A_BYTES + swz(r, kc);
   }
-
-  // wave roles: two 32-row weight blocks x four 32-row activation blocks
-  const int wb0 = SWIGLU ? 32 * w : 64 * w;
-  const int wb1 = SWIGLU ? BNW / 2 + 32 * w : 64 * w + 32;
-  const int ncol0 = SWIGLU ? n0 + 32 * w : n0 + 64 * w;        // output column of block 0
-  const int ncol1 = SWIGLU ? ncol0 : ncol0 + 32;
-  const bool wv0 = ncol0 < Nd;
-  const bool wv1 = ncol1 < Nd;
-  const int xblocks = ceil_div(tm.rows, 32);
-
-  floatx16 acc[2][4];
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds_base = static_cast<uint32_t>((size_t)((lds_char*)lds));  // LDS byte offset
+  auto issue = [&](int ks) {
+    const uint32_t st = lds_base + (ks % STAGES) * STAGE_BYTES + w * 1024;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(src[i] + ks * BK, st + i * 4096);
+  };
+
+  // wave roles: 4 weight blocks of 32 rows x 4 activation blocks of 32 rows
+  int wrow[4], ncol[4];
+  bool wv[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    wrow[b] = SWIGLU ? ((b < 2) ? 64 * w + 32 * b : BN / 2 + 64 * w + 32 * (b - 2)) : 128 * w + 32 * b;
+    ncol[b] = SWIGLU ? n0 + 64 * w + 32 * (b & 1) : n0 + 128 * w + 32 * b;
+    wv[b] = ncol[b] < Nd;
+  }
+  const int xblocks = __builtin_amdgcn_readfirstlane(ceil_div(tm.rows, 32));
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  u32x4 ra[2], rw[4];
   const int nk = Kd / BK;
-  auto gload = [&](int ks) {
-    const int ko = ks * BK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(asrc[i] + ko);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rw[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + ko);
-  };
-  auto lstore = [&](int buf) {
-    char* base = lds + buf * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(base + alds[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + wlds[i]) = rw[i];
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int lr = lane & 31;
   const int lh = lane >> 5;
+  issue(0);
+  if (nk > 1) issue(1);
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) gload(ks + 1);
-    const char* base = lds + (ks & 1) * STAGE_BYTES;
+    // stage ks landed (only stage ks + 1 may still be in flight), visible to all waves;
+    // the barrier also retires every read of the slot that stage ks + 2 overwrites
+    if (ks + 1 < nk) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
+    __syncthreads();
+    if (ks + 2 < nk) issue(ks + 2);
+    const char* st = lds + (ks % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kc = 2 * s + lh;
-      const bf16x8 wa0 = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(base + A_BYTES + swz(wb0 + lr, kc)));
-      const bf16x8 wa1 = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(base + A_BYTES + swz(wb1 + lr, kc)));
+      bf16x8 wa[4], xb[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        wa[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + X_BYTES + swz(wrow[b] + lr, kc)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + swz(32 * j + lr, kc)));
+      // weight blocks past N_dim hold clamped rows: computed, never stored
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j < xblocks) {
-          const bf16x8 xb = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(base + swz(32 * j + lr, kc)));
-          if (wv0) acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa0, xb, acc[0][j], 0, 0, 0);
-          if (wv1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa1, xb, acc[1][j], 0, 0, 0);
-        }
+        if (j >= xblocks) break;  // wave-uniform: activation blocks past the tile's rows
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[b], xb[j], acc[b][j], 0, 0, 0);
       }
     }
-    if (ks + 1 < nk) lstore((ks + 1) & 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds row (32 j + lr) and columns 8 q + 4 lh + {0..3} of each block
@@ -208,19 +172,21 @@ gemm_bf16_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (SWIGLU) {
-        if (!wv0) continue;
-        const int n = ncol0 + 8 * q + 4 * lh;
-        float h[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) h[u] = silu_f(acc[0][j][4 * q + u]) * acc[1][j][4 * q + u];
-        *reinterpret_cast<u32x2*>(orow + n) = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        for (int b = 0; b < 2; ++b) {
+          if (!wv[b]) continue;
+          const int n = ncol[b] + 8 * q + 4 * lh;
+          float h[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) h[u] = silu_f(acc[b][j][4 * q + u]) * acc[b + 2][j][4 * q + u];
+          *reinterpret_cast<u32x2*>(orow + n) = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const bool ok = i == 0 ? wv0 : wv1;
-          if (!ok) continue;
-          const int n = (i == 0 ? ncol0 : ncol1) + 8 * q + 4 * lh;
-          const floatx16& c = acc[i][j];
+        for (int b = 0; b < 4; ++b) {
+          if (!wv[b]) continue;
+          const int n = ncol[b] + 8 * q + 4 * lh;
+          const floatx16& c = acc[b][j];
           *reinterpret_cast<u32x2*>(orow + n) =
               u32x2{pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3])};
         }
@@ -240,13 +206,13 @@ gemm_f32_kernel(int G, int Kd, int Nd, const float* __restrict__ a,
                 const int32_t* __restrict__ offsets, int max_rows, const float* __restrict__ w0,
                 const float* __restrict__ w1, float* __restrict__ out) {
   __shared__ int s_off[kMaxN + 1];
-  __shared__ int s_mstart[THREADS + 1];
+  __shared__ int s_tstart[THREADS + 1];
   __shared__ float sa[FBK][FBM + 4];
   __shared__ float sg[FBK][FBN + 4];
   __shared__ float su[FBK][FBN + 4];
   const int n_tiles = ceil_div(Nd, FBN);
   TileMap tm;
-  if (!decode_tile(offsets, G, max_rows, FBM, n_tiles, s_off, s_mstart, tm)) return;
+  if (!decode_tile(offsets, G, max_rows, FBM, n_tiles, s_off, s_tstart, tm)) return;
   const int tid = threadIdx.x;
   const int n0 = tm.nt * FBN;
   const size_t wstride = static_cast<size_t>(Nd) * Kd;
@@ -293,7 +259,7 @@ hipError_t launch_grouped_gemm(bool swiglu, int G, int Kd, int Nd, int dt, const
                                const int32_t* offsets, int max_rows, const void* w0,
                                const void* w1, void* out, hipStream_t stream) {
   const int bm = dt == 1 ? BM : FBM;
-  const int cols = dt == 1 ? (swiglu ? BNW / 2 : BNW) : FBN;
+  const int cols = dt == 1 ? (swiglu ? BN / 2 : BN) : FBN;
   const int n_tiles = (Nd + cols - 1) / cols;
   const long max_m = static_cast<long>(max_rows) / bm + G + 1;
   long grid = max_m * n_tiles;

@@ -9,8 +9,9 @@
 //   count   one wave per 64-token chunk: each expert's 64-bit token mask is built with
 //           LDS OR (order-free), so a route's rank inside the chunk is a popcount of
 //           the mask below its lane and the chunk histogram is the mask's popcount.
-//   scan    one workgroup: per-expert running sum over chunks (chunk base ranks and
-//           C^req), C^keep = min(C^req, capacity), exclusive scan -> offsets.
+//   scan    one workgroup: per-expert running sums over chunks, split over up to 1024
+//           threads (chunk base ranks and C^req), C^keep = min(C^req, capacity), and an
+//           exclusive scan over experts -> offsets.
 //   scatter one wave per token: rank = chunk base + rank in chunk; kept iff rank <
 //           C^keep; the token's row is read once (16-byte lanes, coalesced) and written
 //           to each kept destination.
@@ -54,52 +55,80 @@ count_kernel(int T, int N, int K, const int32_t* __restrict__ topk_idx,
       hist[static_cast<size_t>(chunk) * N + e] = __popcll(m[e]);
 }
 
-constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_THREADS = 1024;
 
 // Single workgroup. hist[c][e] (chunk counts) is overwritten with the exclusive
 // running sum over chunks, i.e. the rank of chunk c's first route to expert e.
+// Thread t owns expert e = t % NP and the p-th contiguous run of chunks, p = t / NP
+// (NP = N rounded up to a power of two): its loads are independent and coalesced
+// across the experts; a scan over the P runs of each expert then gives the bases.
 __global__ void __launch_bounds__(SCAN_THREADS)
-scan_kernel(int nchunks, int N, int capacity, int32_t* __restrict__ hist,
+scan_kernel(int nchunks, int N, int NP, int capacity, int32_t* __restrict__ hist,
             int32_t* __restrict__ C_req, int32_t* __restrict__ C_keep,
             int32_t* __restrict__ offsets) {
   __shared__ int32_t part[SCAN_THREADS];
+  __shared__ int32_t keep[kMaxN];
   const int tid = threadIdx.x;
-  const int per = (N + SCAN_THREADS - 1) / SCAN_THREADS;  // experts per thread (<= 4)
-  int keep[kMaxN * 4 / SCAN_THREADS];
+  const int P = SCAN_THREADS / NP;
+  const int e = tid % NP, p = tid / NP;
+  const int per = (nchunks + P - 1) / P;
+  const int c0 = min(p * per, nchunks), c1 = min(c0 + per, nchunks);
   int local = 0;
-  for (int j = 0; j < per; ++j) {
-    const int e = tid * per + j;
-    int run = 0;
-    if (e < N) {
-      for (int c = 0; c < nchunks; ++c) {
-        const size_t o = static_cast<size_t>(c) * N + e;
-        const int h = hist[o];
-        hist[o] = run;
-        run += h;
-      }
-      C_req[e] = run;
+  if (e < N) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<size_t>(c + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) local += h[u];
     }
-    const int kk = (e < N) ? ((capacity < 0 || run < capacity) ? run : capacity) : 0;
-    if (e < N) C_keep[e] = kk;
-    keep[j] = kk;
-    local += kk;
+    for (; c < c1; ++c) local += hist[static_cast<size_t>(c) * N + e];
   }
-  // inclusive Hillis-Steele scan of the per-thread totals
   part[tid] = local;
   __syncthreads();
-  for (int off = 1; off < SCAN_THREADS; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+  // exclusive prefix over the runs p' < p of the same expert (P <= 256, serial is fine
+  // for the few runs; done by each thread over its own expert's column of part[])
+  int base = 0;
+  for (int q = 0; q < p; ++q) base += part[q * NP + e];
+  if (e < N) {
+    int run = base;
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {  // batches of independent loads, then the stores
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = hist[static_cast<size_t>(c + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hist[static_cast<size_t>(c + u) * N + e] = run;
+        run += h[u];
+      }
+    }
+    for (; c < c1; ++c) {
+      const size_t o = static_cast<size_t>(c) * N + e;
+      const int h = hist[o];
+      hist[o] = run;
+      run += h;
+    }
+    if (p == P - 1) {
+      C_req[e] = run;
+      const int kk = (capacity < 0 || run < capacity) ? run : capacity;
+      C_keep[e] = kk;
+      keep[e] = kk;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of C_keep over experts (N <= 256): Hillis-Steele in part[0..N)
+  if (tid < kMaxN) part[tid] = (tid < N) ? keep[tid] : 0;
+  __syncthreads();
+  for (int off = 1; off < kMaxN; off <<= 1) {
+    const int v = (tid < kMaxN && tid >= off) ? part[tid - off] : 0;
     __syncthreads();
-    part[tid] += v;
+    if (tid < kMaxN) part[tid] += v;
     __syncthreads();
   }
-  int base = part[tid] - local;
-  for (int j = 0; j < per; ++j) {
-    const int e = tid * per + j;
-    if (e < N) offsets[e] = base;
-    base += keep[j];
-  }
-  if (tid == SCAN_THREADS - 1) offsets[N] = part[tid];
+  if (tid < N) offsets[tid] = part[tid] - keep[tid];
+  if (tid == 0) offsets[N] = part[kMaxN - 1];
 }
 
 constexpr int SC_WAVES = 4;
@@ -162,8 +191,10 @@ hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* h
 hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
                        int32_t* C_keep, int32_t* offsets, hipStream_t stream) {
   const int nchunks = (T + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, nchunks, N, capacity,
-                     hist, C_req, C_keep, offsets);
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, nchunks, N, NP,
+                     capacity, hist, C_req, C_keep, offsets);
   return hipGetLastError();
 }
 

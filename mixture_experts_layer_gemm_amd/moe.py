@@ -32,7 +32,8 @@ class MoEError(RuntimeError):
 class ForwardArgs(ctypes.Structure):
     """Mirror of moe_forward_args."""
     _fields_ = [(n, c_int) for n in ("T", "d_model", "N", "K", "d_r", "d_s", "score", "renorm")] + [
-        ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("dt", c_int)] + [
+        ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("dt", c_int),
+        ("weights_packed", c_int)] + [
         (n, c_void_p) for n in ("x", "w_router", "logit_bias", "w_shared_gate", "w_gate", "w_up",
                                 "w_down", "ws_gate", "ws_up", "ws_down", "y", "logits", "topk_idx",
                                 "topk_r", "s_tok", "C_req", "C_keep", "offsets", "dest_row",
@@ -53,8 +54,9 @@ def _load() -> ctypes.CDLL:
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
-        "moe_grouped_swiglu": (I, [I, I, I, I, P, P, I, P, P, P, P, P, P]),
-        "moe_grouped_gemm": (I, [I, I, I, I, I, P, P, I, P, P, P, P]),
+        "moe_grouped_swiglu": (I, [I, I, I, I, I, P, P, I, P, P, P, P, P, P]),
+        "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, P, I, P, P, P, P]),
+        "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
         "moe_forward": (I, [POINTER(ForwardArgs), P, S, P]),
@@ -173,25 +175,36 @@ def moe_permute(x, topk_idx, N: int, capacity: int = -1):
     return out
 
 
-def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None):
+def moe_pack_weights(w):
+    """[G][N][K] bf16 weights -> the MFMA-operand layout of moe_pack_weights (same shape
+    and dtype; only the element order differs). A one-time weight-load step."""
+    G, N, K = w.shape
+    p = torch.empty_like(w)
+    st = lib.moe_pack_weights(G, N, K, _dt(w), _ptr(w), _ptr(p), _stream())
+    _check("moe_pack_weights", st)
+    return p
+
+
+def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None, packed=False):
     """Grouped SwiGLU over packed segments (offsets=None: one group over all rows)."""
     rows, d = a.shape
     G, d_ff, _ = w_gate.shape
     h = torch.empty(rows, d_ff, dtype=a.dtype, device=a.device) if h is None else h
     out = torch.empty(rows, d, dtype=a.dtype, device=a.device) if out is None else out
-    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), _ptr(a), _ptr(offsets), rows, _ptr(w_gate),
-                                _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out), _stream())
+    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), int(packed), _ptr(a), _ptr(offsets), rows,
+                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out),
+                                _stream())
     _check("moe_grouped_swiglu", st)
     return h, out
 
 
-def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True):
+def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True, packed=False):
     """One grouped GEMM pass: SwiGLU(gate, up) when swiglu, else a plain projection."""
     rows, Kd = a.shape
     G, Nd, _ = w0.shape
     out = torch.empty(rows, Nd, dtype=a.dtype, device=a.device) if out is None else out
-    st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), _ptr(a), _ptr(offsets), rows,
-                              _ptr(w0), _ptr(w1), _ptr(out), _stream())
+    st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), int(packed), _ptr(a),
+                              _ptr(offsets), rows, _ptr(w0), _ptr(w1), _ptr(out), _stream())
     _check("moe_grouped_gemm", st)
     return out
 
@@ -224,27 +237,36 @@ class MoELayer:
 
     def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
-                 logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False):
+                 logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
+                 pack_weights=None):
         self.x = x
         T, d = x.shape
         N, d_r, _ = w_gate.shape
         dev = x.device
-        packed = pack_shared(shared) if shared else None
+        shared_mlp = pack_shared(shared) if shared else None
+        if pack_weights is None:                      # the fast path whenever it applies
+            pack_weights = x.dtype == torch.bfloat16
+        self.weights_packed = bool(pack_weights)
+        if self.weights_packed:
+            w_gate, w_up, w_down = (moe_pack_weights(w) for w in (w_gate, w_up, w_down))
+            if shared_mlp:
+                shared_mlp = tuple(moe_pack_weights(w[None])[0] for w in shared_mlp)
         self.tensors = dict(w_router=w_router, w_gate=w_gate, w_up=w_up, w_down=w_down,
-                            logit_bias=logit_bias, w_shared_gate=w_shared_gate)
-        self.packed = packed
-        d_s = packed[0].shape[0] if packed else 0
+                            logit_bias=logit_bias, w_shared_gate=w_shared_gate)  # kept alive
+        self.shared_mlp = shared_mlp      # (gate, up, down) of the one shared MLP, or None
+        d_s = shared_mlp[0].shape[0] if shared_mlp else 0
         self.y = torch.empty(T, d, dtype=x.dtype, device=dev)
         self.rows = max_rows(T, N, K, capacity)
         self.out = {}
         a = ForwardArgs()
         a.T, a.d_model, a.N, a.K, a.d_r, a.d_s = T, d, N, K, d_r, d_s
         a.score, a.renorm, a.alpha, a.s, a.capacity, a.dt = score, int(renorm), alpha, s, capacity, _dt(x)
+        a.weights_packed = int(self.weights_packed)
         a.x, a.w_router, a.w_gate, a.w_up, a.w_down = (_ptr(x), _ptr(w_router), _ptr(w_gate),
                                                        _ptr(w_up), _ptr(w_down))
         a.logit_bias, a.w_shared_gate = _ptr(logit_bias), _ptr(w_shared_gate)
-        if packed:
-            a.ws_gate, a.ws_up, a.ws_down = (_ptr(p) for p in packed)
+        if shared_mlp:
+            a.ws_gate, a.ws_up, a.ws_down = (_ptr(p) for p in shared_mlp)
         a.y = _ptr(self.y)
         if keep_intermediates:
             rows = max(self.rows, 1)

@@ -206,9 +206,10 @@ class LayerInputs:
         return [tuple(self.as_float(w) for w in ws) for ws in self.shared]
 
 
-def make_inputs(cfg: Config, T: Optional[int] = None) -> LayerInputs:
+def make_inputs(cfg: Config, T: Optional[int] = None, progress=None) -> LayerInputs:
     """Draw every input of `cfg` (optionally with a different token count T, which
-    keeps the same streams, so a smaller T gives a prefix of the same tokens)."""
+    keeps the same streams, so a smaller T gives a prefix of the same tokens).
+    `progress(done, total)` is called as expert weights are drawn."""
     T = cfg.T if T is None else T
     d, N, dr = cfg.d_model, cfg.N, cfg.d_r
     sdt = np.uint16 if cfg.dtype == "bf16" else np.float32
@@ -229,7 +230,9 @@ def make_inputs(cfg: Config, T: Optional[int] = None) -> LayerInputs:
         _draw(cfg, T_DOWN, i, (d, dr), cfg.std_w, out=w_down[i])
 
     with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, range(N)))
+        for i, _ in enumerate(ex.map(one, range(N))):
+            if progress is not None and (i + 1) % 16 == 0:
+                progress(i + 1, N)
     shared = []
     for j, m in enumerate(cfg.shared_widths):
         shared.append((_draw(cfg, T_SGATE, j, (m, d), cfg.std_w),

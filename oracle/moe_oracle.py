@@ -310,30 +310,29 @@ def forward(spec: LayerSpec, x, w_router, expert_weights: Callable[[int], tuple]
 
 def forward_tokens(spec: LayerSpec, tokens, x, idx, r, kept_or_dest, expert_weights,
                    shared_experts: Sequence = (), s_tok=None) -> np.ndarray:
-    """y for a subset of tokens, one token at a time, given that token's routing
-    (selected experts, coefficients and which routes were kept). This is p1 Eq. 80
-    evaluated directly per token, f_i(x) = E_i(x) of p4 Eq. 74, for sampled checks at
-    sizes where the whole layer is too slow on the CPU."""
+    """y for a subset of tokens, given each token's routing (selected experts, their
+    coefficients and which routes were kept): p1 Eq. 80 evaluated directly, with
+    f_i(x) = E_i(x) of p4 Eq. 74, for sampled checks at sizes where the whole layer is
+    too slow on the CPU. Each touched expert's weights are fetched once."""
     x = _f64(x)
     kept = np.asarray(kept_or_dest)
     if kept.dtype != bool:
         kept = kept >= 0
-    cache = {}
-    out = []
-    for t in tokens:
-        xt = x[t:t + 1]
-        yt = np.zeros((1, x.shape[1]))
+    tokens = list(tokens)
+    y = np.zeros((len(tokens), x.shape[1]))
+    uses = {}
+    for j, t in enumerate(tokens):
         for k in range(idx.shape[1]):
             if kept[t, k]:
-                e = int(idx[t, k])
-                if e not in cache:
-                    cache.clear()
-                    cache[e] = expert_weights(e)
-                _, Fe = swiglu(xt, *cache[e])
-                yt += float(r[t, k]) * Fe
-        g = shared_output(xt, shared_experts)
-        if g is not None:
-            gain = float(s_tok[t]) if s_tok is not None else spec.s
-            yt += gain * g
-        out.append(yt[0])
-    return np.stack(out) if out else np.zeros((0, x.shape[1]))
+                uses.setdefault(int(idx[t, k]), []).append((j, t, k))
+    for e in sorted(uses):
+        wg, wu, wd = expert_weights(e)
+        rows = [t for (_, t, _) in uses[e]]
+        _, Fe = swiglu(x[rows], wg, wu, wd)
+        for n, (j, t, k) in enumerate(uses[e]):
+            y[j] += float(r[t, k]) * Fe[n]
+    g = shared_output(x[tokens], shared_experts) if tokens else None
+    if g is not None:
+        gain = np.asarray(s_tok, np.float64)[tokens] if s_tok is not None else spec.s
+        y += (gain[:, None] if np.ndim(gain) else gain) * g
+    return y

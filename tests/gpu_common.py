@@ -54,7 +54,8 @@ class DeviceLayer:
 
     def __init__(self, cfg: synth.Config, T=None):
         self.cfg = cfg
-        self.inp = synth.make_inputs(cfg, T=T)
+        self.inp = synth.make_inputs(
+            cfg, T=T, progress=lambda i, n: say(f"  {cfg.name}: {i}/{n} experts drawn"))
         inp = self.inp
         dt = cfg.dtype
         self.T = inp.x.shape[0]

@@ -122,10 +122,10 @@ def test_permute_stage(name):
 # ---------------------------------------------------------------------------------------
 # a5+a6: grouped SwiGLU GEMM over ragged segments
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,packed", [("bf16", True), ("bf16", False), ("f32", False)])
 @pytest.mark.parametrize("seg", [[0, 1, 129, 0, 400, 31, 256, 257], [300], [0, 0, 5], [1000, 2]])
-def test_grouped_swiglu_ragged(seg, dtype):
-    say(f"grouped swiglu segments={seg} {dtype}")
+def test_grouped_swiglu_ragged(seg, dtype, packed):
+    say(f"grouped swiglu segments={seg} {dtype} packed={packed}")
     rng = np.random.default_rng(len(seg) + sum(seg))
     G, d, dff = len(seg), 192, 320
     rows = sum(seg)
@@ -139,9 +139,11 @@ def test_grouped_swiglu_ragged(seg, dtype):
     a_s = draw((rows + 7, d), 1.0)
     wg_s, wu_s, wd_s = draw((G, dff, d), 0.05), draw((G, dff, d), 0.05), draw((G, d, dff), 0.05)
     dec = (lambda b: synth.bf16_to_f32(b)) if dtype == "bf16" else (lambda b: b)
+    wg_d, wu_d, wd_d = to_device(wg_s, dtype), to_device(wu_s, dtype), to_device(wd_s, dtype)
+    if packed:
+        wg_d, wu_d, wd_d = (moe.moe_pack_weights(w) for w in (wg_d, wu_d, wd_d))
     h, out = moe.moe_grouped_swiglu(to_device(a_s, dtype), torch.from_numpy(offsets).cuda(),
-                                    to_device(wg_s, dtype), to_device(wu_s, dtype),
-                                    to_device(wd_s, dtype))
+                                    wg_d, wu_d, wd_d, packed=packed)
     torch.cuda.synchronize()
     h, out = host(h), host(out)
     for g in range(G):
@@ -278,3 +280,36 @@ def test_forward_edge_cases():
     st = moe.lib.moe_route(0, cfg.d_model, cfg.N, cfg.K, 0, 1, 1.0, 1, x0.data_ptr() or 1,
                            L.w_router.data_ptr(), None, None, None, 0, 1, 1, None, None, None, 0, None)
     assert st == moe.MOE_OK
+
+
+def test_pack_weights_layout_bit_exact():
+    """moe_pack_weights writes w[g][32 nb + (l & 31)][16 kb + 8 (l >> 5) + e] at
+    packed[g][nb][kb][l][e] (the layout documented in include/moe.h)."""
+    rng = np.random.default_rng(3)
+    G, N, K = 3, 128, 192
+    w = rng.integers(0, 1 << 16, size=(G, N, K), dtype=np.uint16)
+    p = host_bits(moe.moe_pack_weights(to_device(w, "bf16")))
+    ref = w.reshape(G, N // 32, 32, K // 16, 2, 8).transpose(0, 1, 3, 4, 2, 5).reshape(G, N, K)
+    assert np.array_equal(p, ref)
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["S_softmax", "S_capgate"])
+def test_forward_row_major_weights(name):
+    """The row-major weight path (no packing) gives the same results."""
+    L = layer(name)
+    c = L.cfg
+    say(f"forward row-major {name}")
+    a = moe.MoELayer(L.x, L.w_router, L.w_gate, L.w_up, L.w_down, c.K, pack_weights=False,
+                     **L.layer_kwargs())
+    b = moe.MoELayer(L.x, L.w_router, L.w_gate, L.w_up, L.w_down, c.K, pack_weights=True,
+                     **L.layer_kwargs())
+    ya = a.forward().float().cpu().numpy()
+    yb = b.forward().float().cpu().numpy()
+    torch.cuda.synchronize()
+    assert rel_l2(ya, yb) <= 2e-3
+    res = L.oracle_forward()
+    assert_close(ya, res.y, c.dtype, "y row-major")
