@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
@@ -244,6 +246,13 @@ def main():
         "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
     }
     torch.cuda.synchronize()
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=x.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = args.copy_probe_mib << 20
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample_tokens, T))
