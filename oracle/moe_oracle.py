@@ -167,9 +167,9 @@ class Permutation:
 
 def permutation(idx, kept, N: int) -> Permutation:
     """Pack kept routes into dense per-expert segments: expert i owns rows
-    [o_i, o_{i+1}) with o given by the cumulative kept counts (p5 Eq. 26, "valid rows
-    packed at the front"); inside a segment rows follow ascending token index.
-    Dropped routes get no row and are masked in restoration and combine (p5 Section
+    [o_i, o_{i+1}) with o given by the cumulative kept counts (p5 Eq. 26: the valid rows
+    sit densely from row 0); inside a segment rows follow ascending token index.
+    Dropped routes get no row and are left out of restoration and combine (p5 Section
     10.3)."""
     idx = np.asarray(idx)
     T, K = idx.shape
@@ -218,8 +218,8 @@ def shared_output(x, shared_experts: Sequence) -> Optional[np.ndarray]:
 def combine(F_perm, dest_row, r, G=None, s=1.0) -> np.ndarray:
     """y_t = sum_{i in S_t, kept} r_{t,i} f_i(x_t) + s_t g(x_t) (p1 Eq. 80), reading each
     expert output from its packed row. Dropped routes contribute nothing and the kept
-    coefficients are not renormalized (p5 Section 10.3: restoration and combine mask
-    the tail-dropped routes). `s` is a scalar gain or a per-token gate vector."""
+    coefficients are not renormalized (p5 Section 10.3: routes that capacity dropped
+    are left out of restoration and combine). `s` is a scalar gain or a per-token gate vector."""
     dest_row = np.asarray(dest_row)
     T, K = dest_row.shape
     F_perm = _f64(F_perm)

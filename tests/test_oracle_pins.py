@@ -162,7 +162,7 @@ def test_coefficient_sums_per_mode():
 
 
 def test_selected_softmax_equals_renormalized_softmax():
-    # exp(z_i)/sum_S exp(z_j) == q_i / sum_S q_j in exact arithmetic (p3's "nearly the same")
+    # exp(z_i)/sum_S exp(z_j) == q_i / sum_S q_j in exact arithmetic (p3 treats the two as slightly different conventions)
     rng = np.random.default_rng(5)
     z = rng.standard_normal((100, 8)) * 3
     idx = O.topk_select(z, 2)
