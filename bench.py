@@ -183,8 +183,10 @@ def main():
     st = {}
     pk = layer.weights_packed
     lw = layer.tensors                 # the layer's own (packed) weights
+    # the gate/up pass gathers its rows from x through row_token, as in moe_forward
     st["gemm_gateup_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
-        o["x_perm"], o["offsets"], lw["w_gate"], lw["w_up"], out=h_perm, swiglu=True, packed=pk), reps)
+        x, o["offsets"], lw["w_gate"], lw["w_up"], out=h_perm, swiglu=True, packed=pk,
+        row_index=o["row_token"]), reps)
     st["gemm_down_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
         h_perm, o["offsets"], lw["w_down"], out=f_perm, swiglu=False, packed=pk), reps)
     sm = layer.shared_mlp
@@ -198,7 +200,8 @@ def main():
         x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
         w_shared_gate=gate, want_counts=False), reps)
     idx = o["topk_idx"]
-    st["permute_ms"] = time_graph(torch, lambda: moe.moe_permute(x, idx, N, cap), reps)
+    st["permute_ms"] = time_graph(torch, lambda: moe.moe_permute(x, idx, N, cap, copy_rows=False),
+                                  reps)
     y2 = torch.empty_like(layer.y)
     st["combine_ms"] = time_graph(torch, lambda: moe.moe_combine(
         f_perm, o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2), reps)
@@ -212,7 +215,8 @@ def main():
     traffic = measured_traffic()
     hbm = {
         "route": (T * d * esz + N * d * esz + T * K * 8) / (st["route_ms"] * 1e-3) / 1e9,
-        "permute": (T * d * esz + R * d * esz + T * K * 16) / (st["permute_ms"] * 1e-3) / 1e9,
+        # count: idx in, ranks out; map: idx + ranks in, dest_row + row_token out
+        "permute": (T * K * 20 + R * 4) / (st["permute_ms"] * 1e-3) / 1e9,
         "combine": (R * d * esz + (2 if layer.shared_mlp is not None else 1) * T * d * esz + T * K * 8)
         / (st["combine_ms"] * 1e-3) / 1e9,
     }

@@ -124,7 +124,9 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
  *   row_token          [max_rows] int32 out: source token of packed rows [0, o_N)
  *   x_perm             [max_rows][d_model] out: x_perm[dest_row[t][k]] = x[t]; expert i
  *                      owns rows [o_i, o_{i+1}), rows in ascending token order; rows at
- *                      and beyond o_N are left untouched
+ *                      and beyond o_N are left untouched. May be NULL: then only the
+ *                      counts and maps are written, and the grouped GEMM gathers its
+ *                      rows from x through row_token instead (no packed copy in HBM)
  *   max_rows           >= moe_max_rows(T, N, K, capacity)
  *   workspace          moe_permute_workspace_size(T, N, K) bytes
  * ------------------------------------------------------------------------------- */
@@ -142,7 +144,12 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
  *     out[r] = h[r] W_d,g                              [d_model]
  *
  *   G                  groups (routed experts; 1 for the shared MLP)
- *   a                  [max_rows][d_model] input rows
+ *   a                  input rows: [max_rows][d_model] when row_index is NULL, else any
+ *                      [rows_a][d_model] array
+ *   row_index          [max_rows] int32 DEVICE array or NULL: packed row r reads input row
+ *                      a[row_index[r]] (the permutation of Section 10 fused into the
+ *                      operand load; pass moe_permute's row_token with a = x), NULL = a[r].
+ *                      Entries of rows in [offsets[0], offsets[G]) must index valid rows of a
  *   offsets            [G+1] int32 DEVICE array, non-decreasing, offsets[G] <= max_rows;
  *                      or NULL for one group covering rows [0, max_rows)
  *   w_gate, w_up       [G][d_ff][d_model]
@@ -156,7 +163,8 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
  * concatenation of the gate/up rows and of the down columns (Section 20 Eq. 75-76).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
-                       const int32_t* offsets, int max_rows, const void* w_gate,
+                       const int32_t* row_index, const int32_t* offsets, int max_rows,
+                       const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream);
 
@@ -169,11 +177,13 @@ int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const v
  *               w1 unused)
  * for rows r of group g in [offsets[g], offsets[g+1]) (Section 20 Eq. 74 over the
  * real-count offsets of Section 10 Eq. 26). K_dim and N_dim are multiples of 64;
- * offsets as in moe_grouped_swiglu.
+ * a, row_index and offsets as in moe_grouped_swiglu (a[r] stands for a[row_index[r]]
+ * when row_index is non-NULL).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
-                     const void* a, const int32_t* offsets, int max_rows, const void* w0,
-                     const void* w1, void* out, hipStream_t stream);
+                     const void* a, const int32_t* row_index, const int32_t* offsets,
+                     int max_rows, const void* w0, const void* w1, void* out,
+                     hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_pack_weights: one-time re-layout of G row-major bf16 weight matrices
@@ -244,7 +254,8 @@ typedef struct moe_forward_args {
   int32_t* offsets;      /* [N+1] */
   int32_t* dest_row;     /* [T][K] */
   int32_t* row_token;    /* [rows] */
-  void* x_perm;          /* [rows][d_model] */
+  void* x_perm;          /* [rows][d_model]; only written when non-NULL: the gate/up pass
+                            gathers its rows from x through row_token */
   void* h_perm;          /* [rows][d_r] */
   void* f_perm;          /* [rows][d_model] */
   void* g;               /* [T][d_model] shared output */

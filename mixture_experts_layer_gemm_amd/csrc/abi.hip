@@ -92,7 +92,7 @@ size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
   w.offsets = a->offsets ? a->offsets : c.take<int32_t>(N + 1);
   w.dest_row = a->dest_row ? a->dest_row : c.take<int32_t>(T * K);
   w.row_token = a->row_token ? a->row_token : c.take<int32_t>(rows);
-  w.x_perm = a->x_perm ? a->x_perm : static_cast<void*>(c.take<char>(rows * d * es));
+  w.x_perm = a->x_perm;  // the gate/up pass gathers rows of x; a copy only on request
   w.h_perm = a->h_perm ? a->h_perm : static_cast<void*>(c.take<char>(rows * a->d_r * es));
   w.f_perm = a->f_perm ? a->f_perm : static_cast<void*>(c.take<char>(rows * d * es));
   if (a->d_s > 0) {
@@ -183,7 +183,7 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_router_dims(T, d_model, N, K));
   MOE_TRY(check_dtype(dt));
-  if (!x || !topk_idx || !C_req || !C_keep || !offsets || !dest_row || !row_token || !x_perm)
+  if (!x || !topk_idx || !C_req || !C_keep || !offsets || !dest_row || !row_token)
     return MOE_ERR_INVALID_ARG;
   if (max_rows < moe_max_rows(T, N, K, capacity)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -198,16 +198,20 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
 }
 
 // one grouped GEMM pass on the row-major or the packed-weight kernel
-static hipError_t gemm_pass(bool swiglu, bool packed, int G, int Kd, int Nd, int dt, const void* a,
-                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
-                     void* out, hipStream_t stream) {
+static hipError_t gemm_pass(bool swiglu, bool packed, int G, int Kd, int Nd, int dt,
+                            const void* a, const int32_t* row_index, const int32_t* offsets,
+                            int max_rows, const void* w0, const void* w1, void* out,
+                            hipStream_t stream) {
   if (packed)
-    return launch_grouped_gemm_packed(swiglu, G, Kd, Nd, a, offsets, max_rows, w0, w1, out, stream);
-  return launch_grouped_gemm(swiglu, G, Kd, Nd, dt, a, offsets, max_rows, w0, w1, out, stream);
+    return launch_grouped_gemm_packed(swiglu, G, Kd, Nd, a, row_index, offsets, max_rows, w0, w1,
+                                      out, stream);
+  return launch_grouped_gemm(swiglu, G, Kd, Nd, dt, a, row_index, offsets, max_rows, w0, w1, out,
+                             stream);
 }
 
 int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
-                       const int32_t* offsets, int max_rows, const void* w_gate,
+                       const int32_t* row_index, const int32_t* offsets, int max_rows,
+                       const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
@@ -218,10 +222,10 @@ int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const v
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w_gate || !w_up || !w_down || !h || !out) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(gemm_pass(true, packed, G, d_model, d_ff, dt, a, offsets, max_rows, w_gate, w_up, h,
-                    stream));
-  MOE_HIP(gemm_pass(false, packed, G, d_ff, d_model, dt, h, offsets, max_rows, w_down, nullptr,
-                    out, stream));
+  MOE_HIP(gemm_pass(true, packed, G, d_model, d_ff, dt, a, row_index, offsets, max_rows, w_gate,
+                    w_up, h, stream));
+  MOE_HIP(gemm_pass(false, packed, G, d_ff, d_model, dt, h, nullptr, offsets, max_rows, w_down,
+                    nullptr, out, stream));
   return MOE_OK;
 }
 
@@ -239,8 +243,9 @@ int moe_pack_weights(int G, int N_dim, int K_dim, int dt, const void* w, void* w
 }
 
 int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
-                     const void* a, const int32_t* offsets, int max_rows, const void* w0,
-                     const void* w1, void* out, hipStream_t stream) {
+                     const void* a, const int32_t* row_index, const int32_t* offsets,
+                     int max_rows, const void* w0, const void* w1, void* out,
+                     hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
   if (G <= 0 || K_dim <= 0 || N_dim <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
   if (swiglu != 0 && swiglu != 1) return MOE_ERR_INVALID_ARG;
@@ -250,8 +255,8 @@ int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w0 || (swiglu && !w1) || !out) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(gemm_pass(swiglu == 1, packed == 1, G, K_dim, N_dim, dt, a, offsets, max_rows, w0,
-                    swiglu ? w1 : nullptr, out, stream));
+  MOE_HIP(gemm_pass(swiglu == 1, packed == 1, G, K_dim, N_dim, dt, a, row_index, offsets,
+                    max_rows, w0, swiglu ? w1 : nullptr, out, stream));
   return MOE_OK;
 }
 
@@ -301,16 +306,16 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
   const bool pk = a->weights_packed == 1;
   if (rows > 0) {
-    MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, w.x_perm, w.offsets, rows, a->w_gate,
-                      a->w_up, w.h_perm, stream));
-    MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, w.offsets, rows, a->w_down,
-                      nullptr, w.f_perm, stream));
+    MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, a->x, w.row_token, w.offsets, rows,
+                      a->w_gate, a->w_up, w.h_perm, stream));
+    MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, nullptr, w.offsets, rows,
+                      a->w_down, nullptr, w.f_perm, stream));
   }
   if (a->d_s > 0) {
-    MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, nullptr, T, a->ws_gate, a->ws_up,
-                      w.h_shared, stream));
-    MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, nullptr, T, a->ws_down,
-                      nullptr, w.g, stream));
+    MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, nullptr, nullptr, T, a->ws_gate,
+                      a->ws_up, w.h_shared, stream));
+    MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, nullptr, nullptr, T,
+                      a->ws_down, nullptr, w.g, stream));
   }
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));

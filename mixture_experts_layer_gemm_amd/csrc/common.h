@@ -66,6 +66,7 @@ hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* h
 hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
                        int32_t* C_keep, int32_t* offsets, hipStream_t stream);
 
+// x_perm == nullptr: restoration map only (no row copy)
 hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* x,
                           const int32_t* topk_idx, const int32_t* hist_base,
                           const int32_t* loc_rank, const int32_t* C_keep,
@@ -73,12 +74,13 @@ hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* 
                           void* x_perm, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(bool swiglu, int G, int K_dim, int N_dim, int dt, const void* a,
-                               const int32_t* offsets, int max_rows, const void* w0,
-                               const void* w1, void* out, hipStream_t stream);
+                               const int32_t* row_index, const int32_t* offsets, int max_rows,
+                               const void* w0, const void* w1, void* out, hipStream_t stream);
 
 hipError_t launch_grouped_gemm_packed(bool swiglu, int G, int K_dim, int N_dim, const void* a,
-                                      const int32_t* offsets, int max_rows, const void* w0p,
-                                      const void* w1p, void* out, hipStream_t stream);
+                                      const int32_t* row_index, const int32_t* offsets,
+                                      int max_rows, const void* w0p, const void* w1p, void* out,
+                                      hipStream_t stream);
 
 hipError_t launch_pack_weights(int G, int N_dim, int K_dim, const void* w, void* w_packed,
                                hipStream_t stream);

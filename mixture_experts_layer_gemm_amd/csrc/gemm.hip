@@ -56,7 +56,8 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_chunk(
 template <bool SWIGLU, bool GROUPED>
 __global__ void __launch_bounds__(THREADS, 1)
 gemm_bf16_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
-                 const int32_t* __restrict__ offsets, int max_rows,
+                 const int32_t* __restrict__ row_index, const int32_t* __restrict__ offsets,
+                 int max_rows,
                  const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
                  uint16_t* __restrict__ out) {
   __shared__ int s_off[kMaxN + 1];
@@ -86,7 +87,9 @@ gemm_bf16_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
     if (slot < X_BYTES / 16) {
       const int r = slot >> 2;
       const int c = swz_chunk(r, slot & 3);
-      src[i] = a + static_cast<size_t>(tm.row0 + min(r, tm.rows - 1)) * Kd + c * 8;
+      int row = tm.row0 + min(r, tm.rows - 1);
+      if (row_index != nullptr) row = row_index[row];
+      src[i] = a + static_cast<size_t>(row) * Kd + c * 8;
     } else {
       const int ws = slot - X_BYTES / 16;
       const int r = ws >> 2;
@@ -203,7 +206,8 @@ constexpr int FBM = 64, FBN = 64, FBK = 16;
 template <bool SWIGLU>
 __global__ void __launch_bounds__(THREADS)
 gemm_f32_kernel(int G, int Kd, int Nd, const float* __restrict__ a,
-                const int32_t* __restrict__ offsets, int max_rows, const float* __restrict__ w0,
+                const int32_t* __restrict__ row_index, const int32_t* __restrict__ offsets,
+                int max_rows, const float* __restrict__ w0,
                 const float* __restrict__ w1, float* __restrict__ out) {
   __shared__ int s_off[kMaxN + 1];
   __shared__ int s_tstart[THREADS + 1];
@@ -223,7 +227,9 @@ gemm_f32_kernel(int G, int Kd, int Nd, const float* __restrict__ a,
   for (int k0 = 0; k0 < Kd; k0 += FBK) {
     for (int i = tid; i < FBM * FBK; i += THREADS) {
       const int r = i / FBK, k = i % FBK;
-      sa[k][r] = a[static_cast<size_t>(tm.row0 + min(r, tm.rows - 1)) * Kd + k0 + k];
+      int row = tm.row0 + min(r, tm.rows - 1);
+      if (row_index != nullptr) row = row_index[row];
+      sa[k][r] = a[static_cast<size_t>(row) * Kd + k0 + k];
       const int n = min(n0 + r, Nd - 1);
       sg[k][r] = wg[static_cast<size_t>(n) * Kd + k0 + k];
       if (SWIGLU) su[k][r] = wu[static_cast<size_t>(n) * Kd + k0 + k];
@@ -256,7 +262,8 @@ gemm_f32_kernel(int G, int Kd, int Nd, const float* __restrict__ a,
 }  // namespace
 
 hipError_t launch_grouped_gemm(bool swiglu, int G, int Kd, int Nd, int dt, const void* a,
-                               const int32_t* offsets, int max_rows, const void* w0,
+                               const int32_t* row_index, const int32_t* offsets, int max_rows,
+                               const void* w0,
                                const void* w1, void* out, hipStream_t stream) {
   const int bm = dt == 1 ? BM : FBM;
   const int cols = dt == 1 ? (swiglu ? BN / 2 : BN) : FBN;
@@ -273,22 +280,22 @@ hipError_t launch_grouped_gemm(bool swiglu, int G, int Kd, int Nd, int dt, const
     uint16_t* O = static_cast<uint16_t*>(out);
     const bool grouped = offsets != nullptr;
     if (swiglu && grouped)
-      hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
     else if (swiglu)
-      hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
     else if (grouped)
-      hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
     else
-      hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   } else {
     const float* A = static_cast<const float*>(a);
     const float* W0 = static_cast<const float*>(w0);
     const float* W1 = static_cast<const float*>(w1);
     float* O = static_cast<float*>(out);
     if (swiglu)
-      hipLaunchKernelGGL(gemm_f32_kernel<true>, g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL(gemm_f32_kernel<true>, g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
     else
-      hipLaunchKernelGGL(gemm_f32_kernel<false>, g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+      hipLaunchKernelGGL(gemm_f32_kernel<false>, g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   }
   return hipGetLastError();
 }

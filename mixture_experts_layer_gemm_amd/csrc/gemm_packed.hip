@@ -141,7 +141,8 @@ __device__ __forceinline__ void tile_body(const TileMap& tm, int Kd, int Nd, int
 template <bool SWIGLU, bool GROUPED>
 __global__ void __launch_bounds__(THREADS, 1)
 gemm_packed_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
-                   const int32_t* __restrict__ offsets, int max_rows,
+                   const int32_t* __restrict__ row_index, const int32_t* __restrict__ offsets,
+                   int max_rows,
                    const uint16_t* __restrict__ w0p, const uint16_t* __restrict__ w1p,
                    uint16_t* __restrict__ out) {
   __shared__ int s_off[kMaxN + 1];
@@ -174,13 +175,16 @@ gemm_packed_kernel(int G, int Kd, int Nd, const uint16_t* __restrict__ a,
     nb = min(nb, Nd / 32 - 1);
     ws[b] = reinterpret_cast<const u32x4*>(base) + static_cast<size_t>(nb) * KB * 64 + lane;
   }
-  // activation DMA: instruction i of wave w fills 1 KB block 4 i + w of a stage
+  // activation DMA: instruction i of wave w fills 1 KB block 4 i + w of a stage; with a
+  // row index the packed row r is gathered from activation row row_index[r]
   const uint16_t* xsrc[XDPW];
 #pragma unroll
   for (int i = 0; i < XDPW; ++i) {
     const int slot = (4 * i + w) * 64 + lane;
     const int r = slot >> 3, c = xswz(r, slot & 7);
-    xsrc[i] = a + static_cast<size_t>(tm.row0 + min(r, tm.rows - 1)) * Kd + c * 8;
+    int src = tm.row0 + min(r, tm.rows - 1);
+    if (row_index != nullptr) src = row_index[src];
+    xsrc[i] = a + static_cast<size_t>(src) * Kd + c * 8;
   }
   const int xblocks = __builtin_amdgcn_readfirstlane(ceil_div(tm.rows, 32));
   switch (xblocks) {
@@ -210,7 +214,8 @@ pack_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p, long piece
 }  // namespace
 
 hipError_t launch_grouped_gemm_packed(bool swiglu, int G, int Kd, int Nd, const void* a,
-                                      const int32_t* offsets, int max_rows, const void* w0p,
+                                      const int32_t* row_index, const int32_t* offsets,
+                                      int max_rows, const void* w0p,
                                       const void* w1p, void* out, hipStream_t stream) {
   const int cols = swiglu ? BN / 2 : BN;
   const int n_tiles = (Nd + cols - 1) / cols;
@@ -224,13 +229,13 @@ hipError_t launch_grouped_gemm_packed(bool swiglu, int G, int Kd, int Nd, const 
   uint16_t* O = static_cast<uint16_t*>(out);
   const bool grouped = offsets != nullptr;
   if (swiglu && grouped)
-    hipLaunchKernelGGL((gemm_packed_kernel<true, true>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+    hipLaunchKernelGGL((gemm_packed_kernel<true, true>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   else if (swiglu)
-    hipLaunchKernelGGL((gemm_packed_kernel<true, false>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+    hipLaunchKernelGGL((gemm_packed_kernel<true, false>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   else if (grouped)
-    hipLaunchKernelGGL((gemm_packed_kernel<false, true>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+    hipLaunchKernelGGL((gemm_packed_kernel<false, true>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   else
-    hipLaunchKernelGGL((gemm_packed_kernel<false, false>), g, b, 0, stream, G, Kd, Nd, A, offsets, max_rows, W0, W1, O);
+    hipLaunchKernelGGL((gemm_packed_kernel<false, false>), g, b, 0, stream, G, Kd, Nd, A, row_index, offsets, max_rows, W0, W1, O);
   return hipGetLastError();
 }
 

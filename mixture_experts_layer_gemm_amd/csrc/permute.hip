@@ -176,6 +176,23 @@ scatter_kernel(int T, int d, int N, int K, const void* __restrict__ x,
   }
 }
 
+// restoration map only (no row copy): one thread per (token, slot)
+__global__ void __launch_bounds__(256)
+map_kernel(int T, int N, int K, const int32_t* __restrict__ topk_idx,
+           const int32_t* __restrict__ base, const int32_t* __restrict__ loc_rank,
+           const int32_t* __restrict__ C_keep, const int32_t* __restrict__ offsets,
+           int32_t* __restrict__ dest_row, int32_t* __restrict__ row_token) {
+  const size_t tk = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tk >= static_cast<size_t>(T) * K) return;
+  const int t = static_cast<int>(tk / K);
+  const int e = topk_idx[tk];
+  const int rank = base[static_cast<size_t>(t / kChunk) * N + e] + loc_rank[tk];
+  int dest = -1;
+  if (rank < C_keep[e]) dest = offsets[e] + rank;
+  dest_row[tk] = dest;
+  if (dest >= 0) row_token[dest] = t;
+}
+
 }  // namespace
 
 hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
@@ -203,6 +220,13 @@ hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* 
                           const int32_t* loc_rank, const int32_t* C_keep,
                           const int32_t* offsets, int32_t* dest_row, int32_t* row_token,
                           void* x_perm, hipStream_t stream) {
+  if (x_perm == nullptr) {
+    const size_t n = static_cast<size_t>(T) * K;
+    hipLaunchKernelGGL(map_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                       stream, T, N, K, topk_idx, hist_base, loc_rank, C_keep, offsets, dest_row,
+                       row_token);
+    return hipGetLastError();
+  }
   const int grid = (T + SC_WAVES - 1) / SC_WAVES;
   if (dt == 1)
     hipLaunchKernelGGL(scatter_kernel<2>, dim3(grid), dim3(SC_WAVES * kWave), 0, stream, T,

@@ -5,11 +5,12 @@
 // score rules, and the router projection of "Shared and Fine-Grained Experts" (a
 // bias-free linear layer from d_model to N).
 //
-// One workgroup (4 waves) owns 16 tokens. Phase 1 computes the 16 x N logit tile: for
-// bf16 with v_mfma_f32_16x16x32_bf16, the d_model reduction split round-robin over the
-// waves in 32-wide steps, operands loaded straight from global memory into the MFMA
-// lane layout (x is streamed once; W_r stays in L2), and the four partial tiles summed
-// in LDS in a fixed order. Phase 2 gives each wave 4 tokens: top-K by K rounds of a
+// One workgroup owns BT tokens (16 with 8 waves for N <= 128, 32 with 4 waves beyond).
+// Phase 1 computes the BT x N logit tile: for bf16 with v_mfma_f32_16x16x32_bf16, the
+// d_model reduction split round-robin over the waves in 32-wide steps, operands loaded
+// straight from global memory into the MFMA lane layout several steps at a time (x is
+// streamed once; W_r stays in L2), and the per-wave partial tiles summed in LDS in a
+// fixed order. Phase 2 gives each wave BT / waves tokens: top-K by K rounds of a
 // wave-wide max over packed (ordered float key, inverted expert index) 64-bit values,
 // which yields the lowest index on ties, then the coefficients in the lanes k < K.
 #include "common.h"
@@ -18,8 +19,6 @@ using namespace moe;
 
 namespace {
 
-constexpr int BT = 16;         // tokens per workgroup
-constexpr int THREADS = 256;   // 4 waves
 
 // Order-preserving map float -> uint32 (larger float, larger key); -0.0 maps like +0.0.
 __device__ __forceinline__ uint32_t ord_key(float f) {
@@ -52,16 +51,22 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + expf(-v)); }
 
 // ---- phase 1, bf16: MFMA logits into part[w][BT][ldz] -----------------------------
-template <int NBT>
+// Wave w owns the 32-wide k steps w, w + WAVES, ...; U steps at a time it first issues
+// every operand load (x rows and router rows, straight into the MFMA lane layout), then
+// the MFMAs, so U * (RB + NB) 16-byte loads per lane are in flight at once.
+template <int BT, int NBT, int WAVES, int U>
 __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                             const uint16_t* __restrict__ wgate, int T, int d, int N, int NB,
                             int t0, float* part, int ldz) {
+  constexpr int RB = BT / 16;  // 16-row token blocks
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int row = lane & 15;
   const int kq = (lane >> 4) * 8;
-  const int tok = min(t0 + row, T - 1);
-  const uint16_t* xr = x + static_cast<size_t>(tok) * d + kq;
+  const uint16_t* xr[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    xr[rb] = x + static_cast<size_t>(min(t0 + 16 * rb + row, T - 1)) * d + kq;
   const uint16_t* br[NBT];
 #pragma unroll
   for (int nb = 0; nb < NBT; ++nb) {
@@ -71,40 +76,62 @@ __device__ void logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __re
     else if (n == N && wgate != nullptr) p = wgate;
     br[nb] = p + kq;
   }
-  floatx4 acc[NBT];
+  floatx4 acc[RB][NBT];
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NBT; ++nb) acc[rb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nks = d / 32;
-  for (int ks = w; ks < nks; ks += 4) {
-    const int k0 = ks * 32;
-    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr + k0));
+  for (int ks0 = w; ks0 < nks; ks0 += WAVES * U) {
+    u32x4 av[U][RB], bv[U][NBT];
 #pragma unroll
-    for (int nb = 0; nb < NBT; ++nb) {
-      if (nb < NB) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(br[nb] + k0));
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int ks = min(ks0 + u * WAVES, nks - 1);  // clamped re-read, results skipped below
+      const int k0 = ks * 32;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) av[u][rb] = *reinterpret_cast<const u32x4*>(xr[rb] + k0);
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb)
+        if (nb < NB) bv[u][nb] = *reinterpret_cast<const u32x4*>(br[nb] + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ks0 + u * WAVES >= nks) break;
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb) {
+        if (nb < NB) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av[u][rb]), __builtin_bit_cast(bf16x8, bv[u][nb]),
+                acc[rb][nb], 0, 0, 0);
+        }
       }
     }
   }
   // D layout of 16x16: lane holds column (lane & 15), rows 4*(lane >> 4) + j.
   float* pw = part + w * BT * ldz;
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) {
-    if (nb < NB) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pw[((lane >> 4) * 4 + j) * ldz + nb * 16 + row] = acc[nb][j];
+    for (int nb = 0; nb < NBT; ++nb) {
+      if (nb < NB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pw[(16 * rb + (lane >> 4) * 4 + j) * ldz + nb * 16 + row] = acc[rb][nb][j];
+      }
     }
-  }
 }
 
 // ---- phase 1, f32: one wave per (token, column) dot product -----------------------
+template <int BT, int WAVES>
 __device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wr,
                            const float* __restrict__ wgate, int T, int d, int N, int ncol,
                            int t0, float* z, int ldz) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  for (int p = w; p < BT * ncol; p += 4) {
+  for (int p = w; p < BT * ncol; p += WAVES) {
     const int t = p / ncol, n = p % ncol;
     const int tok = min(t0 + t, T - 1);
     const float* xr = x + static_cast<size_t>(tok) * d;
@@ -116,16 +143,17 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
   }
 }
 
-template <int NBT>
-__global__ void __launch_bounds__(THREADS)
+template <int BT, int NBT, int WAVES, int U>
+__global__ void __launch_bounds__(WAVES * 64)
 route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
              const void* __restrict__ x, const void* __restrict__ w_router,
              const float* __restrict__ logit_bias, const void* __restrict__ w_gate_vec,
              float* __restrict__ logits, int logits_mode, int32_t* __restrict__ topk_idx,
              float* __restrict__ topk_r, float* __restrict__ s_tok) {
+  constexpr int THREADS = WAVES * 64;
   constexpr int ldz = NBT * 16 + 1;
-  __shared__ float smem[4 * BT * ldz];  // bf16 path: 4 wave partials; else the tile only
-  float* z = smem;  // final logits tile [BT][ldz]; the bf16 path first uses 4 partials
+  __shared__ float smem[WAVES * BT * ldz];  // bf16 path: one partial tile per wave
+  float* z = smem;  // final logits tile [BT][ldz]
   const int t0 = blockIdx.x * BT;
   const int tid = threadIdx.x;
   const bool has_gate = (w_gate_vec != nullptr) && logits_mode == 0;
@@ -138,20 +166,24 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
     }
   } else if (dt == 1) {
     const int NB = (ncol + 15) / 16;
-    logits_bf16<NBT>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                     static_cast<const uint16_t*>(w_gate_vec), T, d, N, NB, t0, smem, ldz);
+    logits_bf16<BT, NBT, WAVES, U>(static_cast<const uint16_t*>(x),
+                                   static_cast<const uint16_t*>(w_router),
+                                   static_cast<const uint16_t*>(w_gate_vec), T, d, N, NB, t0,
+                                   smem, ldz);
     __syncthreads();
+    const int S = BT * ldz;
     for (int i = tid; i < BT * ncol; i += THREADS) {
       const int t = i / ncol, n = i % ncol;
       const int o = t * ldz + n;
-      const int S = BT * ldz;
-      float v = ((smem[o] + smem[S + o]) + smem[2 * S + o]) + smem[3 * S + o];
+      float v = smem[o];  // fixed summation order: wave 0, 1, 2, ...
+#pragma unroll
+      for (int q = 1; q < WAVES; ++q) v += smem[q * S + o];
       if (n < N && logit_bias != nullptr) v += logit_bias[n];
       z[o] = v;
     }
   } else {
-    logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
-               static_cast<const float*>(w_gate_vec), T, d, N, ncol, t0, z, ldz);
+    logits_f32<BT, WAVES>(static_cast<const float*>(x), static_cast<const float*>(w_router),
+                          static_cast<const float*>(w_gate_vec), T, d, N, ncol, t0, z, ldz);
     __syncthreads();
     if (logit_bias != nullptr)
       for (int i = tid; i < BT * N; i += THREADS) z[(i / N) * ldz + i % N] += logit_bias[i % N];
@@ -168,7 +200,7 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   // ---- phase 2: top-K and coefficients, one wave per token --------------------------
   const int lane = tid & 63;
   const int w = tid >> 6;
-  for (int t = w; t < BT; t += 4) {
+  for (int t = w; t < BT; t += WAVES) {
     const int tok = t0 + t;
     if (tok >= T) break;
     const float* zr = z + t * ldz;
@@ -224,15 +256,15 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
 }
 
-template <int NBT>
-hipError_t launch_nbt(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
+template <int BT, int NBT, int WAVES, int U>
+hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
                       const void* x, const void* w_router, const float* logit_bias,
                       const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
                       float* topk_r, float* s_tok, hipStream_t stream) {
   const int grid = (T + BT - 1) / BT;
-  hipLaunchKernelGGL(route_kernel<NBT>, dim3(grid), dim3(THREADS), 0, stream, T, d, N, K,
-                     score, renorm, alpha, dt, x, w_router, logit_bias, w_gate_vec, logits,
-                     logits_mode, topk_idx, topk_r, s_tok);
+  hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U>), dim3(grid), dim3(WAVES * 64), 0, stream,
+                     T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, w_gate_vec,
+                     logits, logits_mode, topk_idx, topk_r, s_tok);
   return hipGetLastError();
 }
 
@@ -244,16 +276,18 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
                         int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream) {
   const int ncol = N + ((w_shared_gate != nullptr && logits_mode == 0) ? 1 : 0);
   const int NB = (ncol + 15) / 16;
-#define MOE_ROUTE_CASE(NBT_)                                                                 \
+  // (tokens per workgroup, column blocks, waves, k steps in flight per wave): small N
+  // uses 16 tokens and 8 waves; large N 32 tokens (router rows re-read half as often)
+#define MOE_ROUTE_CASE(BT_, NBT_, W_, U_)                                                    \
   if (NB <= NBT_)                                                                            \
-    return launch_nbt<NBT_>(T, d_model, N, K, score, renorm, alpha, dt, x, w_router,        \
-                            logit_bias, w_shared_gate, logits, logits_mode, topk_idx, topk_r, \
-                            s_tok, stream);
-  MOE_ROUTE_CASE(1)
-  MOE_ROUTE_CASE(2)
-  MOE_ROUTE_CASE(4)
-  MOE_ROUTE_CASE(8)
-  MOE_ROUTE_CASE(17)
+    return launch_cfg<BT_, NBT_, W_, U_>(T, d_model, N, K, score, renorm, alpha, dt, x,      \
+                                         w_router, logit_bias, w_shared_gate, logits,        \
+                                         logits_mode, topk_idx, topk_r, s_tok, stream);
+  MOE_ROUTE_CASE(16, 1, 8, 8)
+  MOE_ROUTE_CASE(16, 2, 8, 8)
+  MOE_ROUTE_CASE(16, 4, 8, 4)
+  MOE_ROUTE_CASE(16, 8, 8, 2)
+  MOE_ROUTE_CASE(32, 17, 4, 1)
 #undef MOE_ROUTE_CASE
   return hipErrorInvalidValue;
 }

@@ -54,8 +54,8 @@ def _load() -> ctypes.CDLL:
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
-        "moe_grouped_swiglu": (I, [I, I, I, I, I, P, P, I, P, P, P, P, P, P]),
-        "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, P, I, P, P, P, P]),
+        "moe_grouped_swiglu": (I, [I, I, I, I, I, P, P, P, I, P, P, P, P, P, P]),
+        "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, P, P, I, P, P, P, P]),
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
@@ -154,8 +154,9 @@ def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = Tr
     return out
 
 
-def moe_permute(x, topk_idx, N: int, capacity: int = -1):
-    """Counts, capacity admission, offsets, restoration map and packed rows."""
+def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True):
+    """Counts, capacity admission, offsets, restoration map and (copy_rows) the packed
+    rows x_perm; without copy_rows the grouped GEMM gathers rows through row_token."""
     T, d = x.shape
     K = topk_idx.shape[1]
     dev = x.device
@@ -165,7 +166,8 @@ def moe_permute(x, topk_idx, N: int, capacity: int = -1):
                offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
                dest_row=torch.empty(T, K, dtype=torch.int32, device=dev),
                row_token=torch.empty(max(rows, 1), dtype=torch.int32, device=dev),
-               x_perm=torch.empty(max(rows, 1), d, dtype=x.dtype, device=dev))
+               x_perm=(torch.empty(max(rows, 1), d, dtype=x.dtype, device=dev)
+                       if copy_rows else None))
     ws = _workspace(lib.moe_permute_workspace_size(T, N, K), dev)
     st = lib.moe_permute(T, d, N, K, capacity, _dt(x), _ptr(x), _ptr(topk_idx),
                          _ptr(out["C_req"]), _ptr(out["C_keep"]), _ptr(out["offsets"]),
@@ -185,26 +187,34 @@ def moe_pack_weights(w):
     return p
 
 
-def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None, packed=False):
-    """Grouped SwiGLU over packed segments (offsets=None: one group over all rows)."""
-    rows, d = a.shape
+def _rows(a, row_index):
+    return a.shape[0] if row_index is None else row_index.shape[0]
+
+
+def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None, packed=False,
+                       row_index=None):
+    """Grouped SwiGLU over packed segments (offsets=None: one group over all rows).
+    With row_index, packed row r reads a[row_index[r]]."""
+    rows, d = _rows(a, row_index), a.shape[1]
     G, d_ff, _ = w_gate.shape
     h = torch.empty(rows, d_ff, dtype=a.dtype, device=a.device) if h is None else h
     out = torch.empty(rows, d, dtype=a.dtype, device=a.device) if out is None else out
-    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), int(packed), _ptr(a), _ptr(offsets), rows,
+    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), int(packed), _ptr(a), _ptr(row_index),
+                                _ptr(offsets), rows,
                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out),
                                 _stream())
     _check("moe_grouped_swiglu", st)
     return h, out
 
 
-def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True, packed=False):
+def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True, packed=False,
+                     row_index=None):
     """One grouped GEMM pass: SwiGLU(gate, up) when swiglu, else a plain projection."""
-    rows, Kd = a.shape
+    rows, Kd = _rows(a, row_index), a.shape[1]
     G, Nd, _ = w0.shape
     out = torch.empty(rows, Nd, dtype=a.dtype, device=a.device) if out is None else out
     st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), int(packed), _ptr(a),
-                              _ptr(offsets), rows, _ptr(w0), _ptr(w1), _ptr(out), _stream())
+                              _ptr(row_index), _ptr(offsets), rows, _ptr(w0), _ptr(w1), _ptr(out), _stream())
     _check("moe_grouped_gemm", st)
     return out
 
@@ -238,7 +248,7 @@ class MoELayer:
     def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
                  logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
-                 pack_weights=None):
+                 pack_weights=None, keep_x_perm=False):
         self.x = x
         T, d = x.shape
         N, d_r, _ = w_gate.shape
@@ -274,8 +284,9 @@ class MoELayer:
             spec = dict(logits=((T, N), f32), topk_idx=((T, K), i32), topk_r=((T, K), f32),
                         C_req=((N,), i32), C_keep=((N,), i32), offsets=((N + 1,), i32),
                         dest_row=((T, K), i32), row_token=((rows,), i32),
-                        x_perm=((rows, d), x.dtype), h_perm=((rows, d_r), x.dtype),
-                        f_perm=((rows, d), x.dtype))
+                        h_perm=((rows, d_r), x.dtype), f_perm=((rows, d), x.dtype))
+            if keep_x_perm:     # an extra copy: the gate/up pass itself gathers from x
+                spec["x_perm"] = ((rows, d), x.dtype)
             if w_shared_gate is not None:
                 spec["s_tok"] = ((T,), f32)
             if d_s:

@@ -55,8 +55,9 @@ def test_workspace_sizes_are_positive_and_monotone():
     args.capacity, args.dt = -1, moe.MOE_BF16
     ws = moe.lib.moe_forward_workspace_size(ctypes.byref(args))
     rows = 4 * 4096
-    # x_perm + h_perm + f_perm + g + shared h dominate
-    assert ws >= 2 * (rows * 2048 * 2 + rows * 2560 + 4096 * 2048 + 4096 * 1280)
+    # h_perm + f_perm + g + shared h dominate (no x_perm: the gate/up pass gathers from x)
+    need = 2 * (rows * 2048 + rows * 2560 + 4096 * 2048 + 4096 * 1280)
+    assert need <= ws < need + 2 * rows * 2048
 
 
 def _route(**kw):
@@ -92,11 +93,11 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, None, 0, None) == \
         moe.MOE_ERR_WORKSPACE
     assert L.moe_permute(0, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, None, 0, None) == moe.MOE_OK
-    assert L.moe_grouped_swiglu(2, 64, 100, 1, 0, 1, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_grouped_swiglu(2, 64, 128, 1, 0, 1, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_grouped_swiglu(1, 64, 128, 1, 0, 1, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
-    assert L.moe_grouped_swiglu(1, 64, 128, 0, 1, 1, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 2, 1, None, 8, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_swiglu(2, 64, 100, 1, 0, 1, None, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_swiglu(2, 64, 128, 1, 0, 1, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_swiglu(1, 64, 128, 1, 0, 1, None, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
+    assert L.moe_grouped_swiglu(1, 64, 128, 0, 1, 1, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 2, 1, None, None, 8, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
     assert L.moe_pack_weights(2, 96, 128, 1, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # N % 64
     assert L.moe_pack_weights(2, 64, 128, 1, 4096, 4096 + 100, None) == moe.MOE_ERR_INVALID_ARG  # overlap

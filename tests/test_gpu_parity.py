@@ -95,15 +95,17 @@ def test_route_stage(name):
 # ---------------------------------------------------------------------------------------
 # a3+a4: counts, capacity, offsets, restoration map and packed rows
 # ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("copy_rows", [True, False])
 @pytest.mark.parametrize("name", SMALL)
-def test_permute_stage(name):
+def test_permute_stage(name, copy_rows):
     L = layer(name)
     c = L.cfg
-    say(f"permute {name} capacity={L.capacity}")
+    say(f"permute {name} capacity={L.capacity} copy_rows={copy_rows}")
     inp = L.inp
     z = O.router_logits(L.x_f(), inp.as_float(inp.w_router), inp.logit_bias)
     idx = O.topk_select(z, c.K)
-    out = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity)
+    out = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity,
+                          copy_rows=copy_rows)
     torch.cuda.synchronize()
     kept = O.keep_routes(idx, c.N, L.capacity)
     perm = O.permutation(idx, kept, c.N)
@@ -113,6 +115,9 @@ def test_permute_stage(name):
     assert np.array_equal(host(out["offsets"]), perm.offsets)
     assert np.array_equal(host(out["dest_row"]), perm.dest_row)
     assert np.array_equal(host(out["row_token"])[:R], perm.row_token)
+    if not copy_rows:
+        assert out["x_perm"] is None
+        return
     xp = out["x_perm"][:R]
     xs = L.x[torch.from_numpy(perm.row_token).long().cuda()]
     assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
@@ -155,6 +160,44 @@ def test_grouped_swiglu_ragged(seg, dtype, packed):
         assert_close(out[lo:hi], F, dtype, f"F segment {g}")
 
 
+@pytest.mark.parametrize("dtype,packed", [("bf16", True), ("bf16", False), ("f32", False)])
+def test_grouped_swiglu_gathered_rows(dtype, packed):
+    """Packed row r of the gate/up pass reads a[row_index[r]] (the permutation fused into
+    the operand load): ragged groups, repeated and out-of-order source rows."""
+    say(f"grouped swiglu gathered rows {dtype} packed={packed}")
+    rng = np.random.default_rng(11)
+    seg = [0, 77, 130, 1, 0, 258]
+    G, d, dff = len(seg), 128, 192
+    rows = sum(seg)
+    offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int32)
+    n_src = 150
+    row_index = rng.integers(0, n_src, size=rows + 5).astype(np.int32)
+
+    def draw(shape, std):
+        v = (rng.standard_normal(shape) * std).astype(np.float32)
+        return synth.bf16_bits(v) if dtype == "bf16" else v
+
+    a_s = draw((n_src, d), 1.0)
+    wg_s, wu_s, wd_s = draw((G, dff, d), 0.05), draw((G, dff, d), 0.05), draw((G, d, dff), 0.05)
+    dec = (lambda b: synth.bf16_to_f32(b)) if dtype == "bf16" else (lambda b: b)
+    wg_d, wu_d, wd_d = to_device(wg_s, dtype), to_device(wu_s, dtype), to_device(wd_s, dtype)
+    if packed:
+        wg_d, wu_d, wd_d = (moe.moe_pack_weights(w) for w in (wg_d, wu_d, wd_d))
+    h, out = moe.moe_grouped_swiglu(to_device(a_s, dtype), torch.from_numpy(offsets).cuda(),
+                                    wg_d, wu_d, wd_d, packed=packed,
+                                    row_index=torch.from_numpy(row_index).cuda())
+    torch.cuda.synchronize()
+    assert h.shape[0] == rows + 5
+    h, out = host(h), host(out)
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi == lo:
+            continue
+        H, F = O.swiglu(dec(a_s[row_index[lo:hi]]), dec(wg_s[g]), dec(wu_s[g]), dec(wd_s[g]))
+        assert_close(h[lo:hi], H, dtype, f"H segment {g}")
+        assert_close(out[lo:hi], F, dtype, f"F segment {g}")
+
+
 # ---------------------------------------------------------------------------------------
 # a8: combine
 # ---------------------------------------------------------------------------------------
@@ -187,12 +230,12 @@ def test_combine_stage(name):
 # ---------------------------------------------------------------------------------------
 # whole layer, small workloads: every intermediate against the oracle
 # ---------------------------------------------------------------------------------------
-def check_forward(L: DeviceLayer, full=True, sample_tokens=None):
+def check_forward(L: DeviceLayer, full=True, sample_tokens=None, keep_x_perm=False):
     c = L.cfg
     dt = c.dtype
-    say(f"forward {c.name} T={L.T} capacity={L.capacity}")
+    say(f"forward {c.name} T={L.T} capacity={L.capacity} keep_x_perm={keep_x_perm}")
     lay = moe.MoELayer(L.x, L.w_router, L.w_gate, L.w_up, L.w_down, c.K,
-                       keep_intermediates=True, **L.layer_kwargs())
+                       keep_intermediates=True, keep_x_perm=keep_x_perm, **L.layer_kwargs())
     y = lay.forward()
     torch.cuda.synchronize()
     o = lay.out
@@ -220,8 +263,11 @@ def check_forward(L: DeviceLayer, full=True, sample_tokens=None):
     assert np.array_equal(host(o["offsets"]), perm.offsets)
     assert np.array_equal(host(o["dest_row"]), perm.dest_row)
     assert np.array_equal(host(o["row_token"])[:R], perm.row_token)
-    row_tok = torch.from_numpy(perm.row_token).long().cuda()
-    assert torch.equal(o["x_perm"][:R], L.x[row_tok])
+    if keep_x_perm:
+        row_tok = torch.from_numpy(perm.row_token).long().cuda()
+        assert torch.equal(o["x_perm"][:R], L.x[row_tok])
+    else:
+        assert "x_perm" not in o
     say(f"  routing bit-exact; R={R} kept of {c.K * L.T}")
     if full:
         Hg, Fg = host(o["h_perm"])[:R], host(o["f_perm"])[:R]
@@ -247,6 +293,11 @@ def check_forward(L: DeviceLayer, full=True, sample_tokens=None):
 @pytest.mark.parametrize("name", SMALL)
 def test_forward_small(name):
     check_forward(layer(name))
+
+
+@pytest.mark.parametrize("name", ["S_capgate", "S_f32"])
+def test_forward_with_x_perm_copy(name):
+    check_forward(layer(name), keep_x_perm=True)
 
 
 def test_forward_is_deterministic():

@@ -66,7 +66,7 @@ def test_full_layer_sampled(name):
     offs = host(o["offsets"])
     Hg = o["h_perm"]
     Fg = o["f_perm"]
-    xp = o["x_perm"]
+    row_token = o["row_token"]
     c = L.cfg
     experts = sorted(set(rng.choice(c.N, size=min(4, c.N), replace=False).tolist()))
     for e in experts:
@@ -75,7 +75,7 @@ def test_full_layer_sampled(name):
             continue
         rows = sorted(set(rng.integers(lo, hi, size=min(16, hi - lo)).tolist()))
         ri = torch.tensor(rows, device="cuda")
-        X = host(xp[ri])
+        X = host(L.x[row_token[ri].long()])
         H, F = O.swiglu(X, *L.inp.expert_f32(e))
         assert_close(host(Hg[ri]), H, "bf16", f"H rows of expert {e}")
         assert_close(host(Fg[ri]), F, "bf16", f"F rows of expert {e}")
