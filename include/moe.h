@@ -144,8 +144,9 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
  *     out[r] = h[r] W_d,g                              [d_model]
  *
  *   G                  groups (routed experts; 1 for the shared MLP)
- *   a                  input rows: [max_rows][d_model] when row_index is NULL, else any
- *                      [rows_a][d_model] array
+ *   a                  input rows: [max_rows][d_model] when row_index is NULL, else
+ *                      [a_rows][d_model]
+ *   a_rows             rows of a when row_index is given (> every entry), else ignored
  *   row_index          [max_rows] int32 DEVICE array or NULL: packed row r reads input row
  *                      a[row_index[r]] (the permutation of Section 10 fused into the
  *                      operand load; pass moe_permute's row_token with a = x), NULL = a[r].
@@ -163,8 +164,8 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
  * concatenation of the gate/up rows and of the down columns (Section 20 Eq. 75-76).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
-                       const int32_t* row_index, const int32_t* offsets, int max_rows,
-                       const void* w_gate,
+                       int a_rows, const int32_t* row_index, const int32_t* offsets,
+                       int max_rows, const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream);
 
@@ -177,13 +178,13 @@ int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const v
  *               w1 unused)
  * for rows r of group g in [offsets[g], offsets[g+1]) (Section 20 Eq. 74 over the
  * real-count offsets of Section 10 Eq. 26). K_dim and N_dim are multiples of 64;
- * a, row_index and offsets as in moe_grouped_swiglu (a[r] stands for a[row_index[r]]
+ * a, a_rows, row_index and offsets as in moe_grouped_swiglu (a[r] stands for a[row_index[r]]
  * when row_index is non-NULL).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
-                     const void* a, const int32_t* row_index, const int32_t* offsets,
-                     int max_rows, const void* w0, const void* w1, void* out,
-                     hipStream_t stream);
+                     const void* a, int a_rows, const int32_t* row_index,
+                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                     void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_pack_weights: one-time re-layout of G row-major bf16 weight matrices

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_packed.hip", "combine.hip", "abi.hip"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_packed.hip", "gemm_stream.hip", "combine.hip",
+           "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

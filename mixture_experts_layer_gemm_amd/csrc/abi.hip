@@ -7,6 +7,7 @@
 
 #include "../../include/moe.h"
 #include "common.h"
+#include "gemm_stream.h"
 
 namespace {
 
@@ -197,21 +198,44 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const vo
   return MOE_OK;
 }
 
-// one grouped GEMM pass on the row-major or the packed-weight kernel
+static StreamProblem problem(const void* a, int a_rows, const int32_t* row_index,
+                             const int32_t* offsets, int G, int rows, int Kd, int Nd,
+                             const void* w0, const void* w1, void* out) {
+  StreamProblem p;
+  p.a = static_cast<const uint16_t*>(a);
+  p.row_index = row_index;
+  p.offsets = offsets;
+  p.G = G;
+  p.rows = rows;
+  p.a_rows = row_index != nullptr ? a_rows : rows;
+  p.Kd = Kd;
+  p.Nd = Nd;
+  p.w0 = static_cast<const uint16_t*>(w0);
+  p.w1 = static_cast<const uint16_t*>(w1);
+  p.out = static_cast<uint16_t*>(out);
+  return p;
+}
+
+// one grouped GEMM pass: the persistent packed-weight kernel where the shape fits it,
+// else the per-tile packed kernel, or the row-major kernels for row-major weights
 static hipError_t gemm_pass(bool swiglu, bool packed, int G, int Kd, int Nd, int dt,
-                            const void* a, const int32_t* row_index, const int32_t* offsets,
-                            int max_rows, const void* w0, const void* w1, void* out,
-                            hipStream_t stream) {
-  if (packed)
+                            const void* a, int a_rows, const int32_t* row_index,
+                            const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                            void* out, hipStream_t stream) {
+  if (packed) {
+    const StreamProblem p0 = problem(a, a_rows, row_index, offsets, G, max_rows, Kd, Nd, w0, w1, out);
+    StreamProblem none{};
+    if (stream_gemm_supported(swiglu, p0, none)) return launch_stream_gemm(swiglu, p0, none, stream);
     return launch_grouped_gemm_packed(swiglu, G, Kd, Nd, a, row_index, offsets, max_rows, w0, w1,
                                       out, stream);
+  }
   return launch_grouped_gemm(swiglu, G, Kd, Nd, dt, a, row_index, offsets, max_rows, w0, w1, out,
                              stream);
 }
 
 int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
-                       const int32_t* row_index, const int32_t* offsets, int max_rows,
-                       const void* w_gate,
+                       int a_rows, const int32_t* row_index, const int32_t* offsets,
+                       int max_rows, const void* w_gate,
                        const void* w_up, const void* w_down, void* h, void* out,
                        hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
@@ -221,11 +245,12 @@ int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const v
   if (G > moe::kMaxN || d_model % 64 != 0 || d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w_gate || !w_up || !w_down || !h || !out) return MOE_ERR_INVALID_ARG;
+  if (row_index != nullptr && a_rows <= 0) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(gemm_pass(true, packed, G, d_model, d_ff, dt, a, row_index, offsets, max_rows, w_gate,
-                    w_up, h, stream));
-  MOE_HIP(gemm_pass(false, packed, G, d_ff, d_model, dt, h, nullptr, offsets, max_rows, w_down,
-                    nullptr, out, stream));
+  MOE_HIP(gemm_pass(true, packed, G, d_model, d_ff, dt, a, a_rows, row_index, offsets, max_rows,
+                    w_gate, w_up, h, stream));
+  MOE_HIP(gemm_pass(false, packed, G, d_ff, d_model, dt, h, max_rows, nullptr, offsets, max_rows,
+                    w_down, nullptr, out, stream));
   return MOE_OK;
 }
 
@@ -243,9 +268,9 @@ int moe_pack_weights(int G, int N_dim, int K_dim, int dt, const void* w, void* w
 }
 
 int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed,
-                     const void* a, const int32_t* row_index, const int32_t* offsets,
-                     int max_rows, const void* w0, const void* w1, void* out,
-                     hipStream_t stream) {
+                     const void* a, int a_rows, const int32_t* row_index,
+                     const int32_t* offsets, int max_rows, const void* w0, const void* w1,
+                     void* out, hipStream_t stream) {
   MOE_TRY(check_dtype(dt));
   if (G <= 0 || K_dim <= 0 || N_dim <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARG;
   if (swiglu != 0 && swiglu != 1) return MOE_ERR_INVALID_ARG;
@@ -254,8 +279,9 @@ int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed
   if (G > moe::kMaxN || K_dim % 64 != 0 || N_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (offsets == nullptr && G != 1) return MOE_ERR_INVALID_ARG;
   if (!a || !w0 || (swiglu && !w1) || !out) return MOE_ERR_INVALID_ARG;
+  if (row_index != nullptr && a_rows <= 0) return MOE_ERR_INVALID_ARG;
   if (max_rows == 0) return MOE_OK;
-  MOE_HIP(gemm_pass(swiglu == 1, packed == 1, G, K_dim, N_dim, dt, a, row_index, offsets,
+  MOE_HIP(gemm_pass(swiglu == 1, packed == 1, G, K_dim, N_dim, dt, a, a_rows, row_index, offsets,
                     max_rows, w0, swiglu ? w1 : nullptr, out, stream));
   return MOE_OK;
 }
@@ -305,17 +331,37 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
   const bool pk = a->weights_packed == 1;
-  if (rows > 0) {
-    MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, a->x, w.row_token, w.offsets, rows,
-                      a->w_gate, a->w_up, w.h_perm, stream));
-    MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, nullptr, w.offsets, rows,
-                      a->w_down, nullptr, w.f_perm, stream));
+  // routed experts (p0) and the shared MLP (p1) in one persistent launch per pass when
+  // the shapes fit it
+  bool fused = false;
+  if (pk && rows > 0 && a->d_s > 0) {
+    const StreamProblem gu0 = problem(a->x, T, w.row_token, w.offsets, N, rows, d, a->d_r,
+                                      a->w_gate, a->w_up, w.h_perm);
+    const StreamProblem gu1 = problem(a->x, T, nullptr, nullptr, 1, T, d, a->d_s, a->ws_gate,
+                                      a->ws_up, w.h_shared);
+    const StreamProblem dn0 = problem(w.h_perm, rows, nullptr, w.offsets, N, rows, a->d_r, d,
+                                      a->w_down, nullptr, w.f_perm);
+    const StreamProblem dn1 = problem(w.h_shared, T, nullptr, nullptr, 1, T, a->d_s, d,
+                                      a->ws_down, nullptr, w.g);
+    if (stream_gemm_supported(true, gu0, gu1) && stream_gemm_supported(false, dn0, dn1)) {
+      MOE_HIP(launch_stream_gemm(true, gu0, gu1, stream));
+      MOE_HIP(launch_stream_gemm(false, dn0, dn1, stream));
+      fused = true;
+    }
   }
-  if (a->d_s > 0) {
-    MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, nullptr, nullptr, T, a->ws_gate,
-                      a->ws_up, w.h_shared, stream));
-    MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, nullptr, nullptr, T,
-                      a->ws_down, nullptr, w.g, stream));
+  if (!fused) {
+    if (rows > 0) {
+      MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, a->x, T, w.row_token, w.offsets, rows,
+                        a->w_gate, a->w_up, w.h_perm, stream));
+      MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, rows, nullptr, w.offsets,
+                        rows, a->w_down, nullptr, w.f_perm, stream));
+    }
+    if (a->d_s > 0) {
+      MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, T, nullptr, nullptr, T, a->ws_gate,
+                        a->ws_up, w.h_shared, stream));
+      MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, T, nullptr, nullptr, T,
+                        a->ws_down, nullptr, w.g, stream));
+    }
   }
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));

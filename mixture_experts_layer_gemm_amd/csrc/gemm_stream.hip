@@ -1,0 +1,442 @@
+// Persistent grouped GEMM with fused SwiGLU over packed weights; the weight stream is
+// prefetched several stages ahead and continues across tile boundaries.
+//
+// Operation and weight layout are those of gemm_packed.hip (expert i owns packed rows
+// [o_i, o_{i+1}), "Section 10: Routing, Capacity, and Load Balancing", Eq. 26; the SwiGLU
+// expert of "Section 20: One Shared Expert Is All You Need", Eq. 74; weights in the
+// v_mfma_f32_32x32x16_bf16 A-operand order written by moe_pack_weights). One launch
+// serves up to two problems: a grouped one (the routed experts over their real-count
+// segments, activation rows optionally gathered through a row index) and a dense one
+// (the shared MLP over all tokens), so the shared expert fills the routed pass's tail.
+//
+// Schedule (one workgroup of 4 waves per compute unit):
+//   * tiles are ordered (problem, group, n-tile, m-tile); the 8 contiguous eighths of
+//     that list go to the 8 XCDs (workgroup b runs on XCD b % 8) and the workgroups of
+//     an XCD take every (grid / 8)-th tile of its eighth, so the row tiles that share a
+//     weight block run at the same time behind the same L2;
+//   * every wave streams its NBW weight blocks straight into registers, RS stages
+//     (64 k each) ahead, in a register ring; activations go through a 4-stage LDS ring
+//     filled by direct-to-LDS loads; in the last stages of a tile both rings are already
+//     refilled with the next tile's first stages, so the pipeline never drains;
+//   * these loads are not visible to the compiler (inline asm): every stage issues the
+//     same number of them, and one explicit s_waitcnt vmcnt per stage, before the stage
+//     barrier, covers the weights and activations that stage consumes. Other memory
+//     operations (epilogue stores, row-index loads) only add to the count, which can
+//     only make that wait stricter.
+// Wave w of a tile owns weight blocks (32 rows each) w * NBW .. w * NBW + NBW - 1 of the
+// tile's 128 NBW weight rows (SwiGLU: NBW / 2 gate blocks and the matching up blocks)
+// and all BM = 32 XBM activation rows.
+#include <utility>
+
+#include "gemm_common.h"
+#include "gemm_stream.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int SK_THREADS = 256;
+constexpr int SK_BKX = 64;           // k per stage
+constexpr int SK_XS = 4;             // activation ring depth (stages)
+constexpr int SK_SPS = SK_BKX / 16;  // k16 steps per stage
+
+// physical 16-byte chunk of logical chunk c (0..7) of activation row r in a stage:
+// conflict-free MFMA operand reads
+__device__ __forceinline__ int sk_swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+// direct-to-LDS loads (uniform base + 32-bit per-lane byte offset; lane j lands at
+// lds_addr + j * size)
+__device__ __forceinline__ void sk_dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void sk_dma4(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+// 16-byte load into registers that the compiler does not track: the register is read
+// only after the stage wait that covers it
+__device__ __forceinline__ void sk_ldg16(u32x4& dst, const void* sbase, uint32_t voff) {
+  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(dst) : "v"(voff), "s"(sbase) : "memory");
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void sk_unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order
+template <int N, typename F>
+__device__ __forceinline__ void sk_unroll(F&& f) {
+  sk_unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int NBW, int XBM, int RS>
+struct SK {
+  static constexpr int BM = 32 * XBM;
+  static constexpr int COLS_SWIGLU = 64 * NBW;   // output columns of a SwiGLU tile
+  static constexpr int COLS_PLAIN = 128 * NBW;
+  static constexpr int XSTAGE = BM * SK_BKX * 2;  // bytes
+  static constexpr int XDPW = XSTAGE / 4096;      // direct-to-LDS loads per wave per stage
+  static constexpr int WPS = SK_SPS * NBW;        // weight loads per wave per stage
+  static constexpr int PER = XDPW + WPS;          // vector memory ops per wave per stage
+  // ops issued after the weights (resp. activations) of stage s when stage s begins
+  static constexpr int AFTER_W = (RS - 1) * PER;
+  static constexpr int AFTER_X = WPS + (SK_XS - 2) * PER;
+  static constexpr int WAITN = AFTER_W < AFTER_X ? AFTER_W : AFTER_X;
+  static_assert(WAITN <= 63, "vmcnt range");
+  static_assert(XDPW * 4096 == XSTAGE, "whole direct-to-LDS loads per stage");
+  static_assert(BM <= 256, "row index buffer");
+};
+
+// one tile, all fields uniform
+struct SkTile {
+  int p;     // problem
+  int g;     // group within the problem
+  int row0;  // first packed row
+  int rows;  // packed rows (1..BM)
+  int n0;    // first output column
+  int nst;   // k stages
+};
+
+template <int NBW, int XBM, int RS, bool SWIGLU>
+__global__ void __launch_bounds__(SK_THREADS, 1)
+gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
+  using C = SK<NBW, XBM, RS>;
+  constexpr int COLS = SWIGLU ? C::COLS_SWIGLU : C::COLS_PLAIN;
+  __shared__ int s_off[kMaxN + 2];     // packed row offsets of the groups (p1 last)
+  __shared__ int s_tstart[SK_THREADS + 1];
+  __shared__ int s_rows[2][256];       // gathered activation rows of the current / next tile
+  __shared__ __attribute__((aligned(1024))) char lds[SK_XS * C::XSTAGE];
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int tid = threadIdx.x;
+  const int G0 = p0.G;
+  const int NG = G0 + (p1.rows > 0 ? 1 : 0);  // groups over both problems (<= 256)
+
+  // ---- tile list: per-group tile counts, prefix-summed in LDS ----
+  for (int g = tid; g <= G0; g += SK_THREADS)
+    s_off[g] = (p0.offsets != nullptr) ? p0.offsets[g] : (g == 0 ? 0 : p0.rows);
+  __syncthreads();
+  if (tid == 0) s_off[G0 + 1] = s_off[G0] + p1.rows;
+  __syncthreads();
+  {
+    int cnt = 0;
+    if (tid < G0) cnt = ceil_div(s_off[tid + 1] - s_off[tid], C::BM) * (p0.Nd / COLS);
+    else if (tid == G0 && NG > G0) cnt = ceil_div(p1.rows, C::BM) * (p1.Nd / COLS);
+    s_tstart[tid + 1] = cnt;
+  }
+  if (tid == 0) s_tstart[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < SK_THREADS; off <<= 1) {  // inclusive scan over <= 256 groups
+    const int v = (tid >= off) ? s_tstart[tid + 1 - off] : 0;
+    __syncthreads();
+    s_tstart[tid + 1] += v;
+    __syncthreads();
+  }
+  const int total = s_tstart[NG];
+  const int step = gridDim.x >> 3;
+  const int seg = ceil_div(total, 8);
+  const int xcd = blockIdx.x & 7;
+  const int t_end = min(total, (xcd + 1) * seg);
+  int t = xcd * seg + (blockIdx.x >> 3);
+  if (t >= t_end) return;
+
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds_base = static_cast<uint32_t>((size_t)((lds_char*)lds));
+  const uint32_t rows_base = static_cast<uint32_t>((size_t)((lds_char*)(&s_rows[0][0])));
+
+  auto tile_at = [&](int ti) -> SkTile {
+    int lo = 0, hi = NG - 1;  // largest g with s_tstart[g] <= ti (a non-empty group)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= ti) lo = mid; else hi = mid - 1;
+    }
+    const bool second = lo >= G0;
+    const int base = second ? 0 : s_off[lo];
+    const int nrows = s_off[lo + 1] - s_off[lo];
+    const int local = ti - s_tstart[lo];
+    const int mtiles = ceil_div(nrows, C::BM);
+    const int nt = local / mtiles;
+    const int mt = local - nt * mtiles;
+    SkTile k;
+    k.p = __builtin_amdgcn_readfirstlane(second ? 1 : 0);
+    k.g = __builtin_amdgcn_readfirstlane(second ? 0 : lo);
+    k.row0 = __builtin_amdgcn_readfirstlane(base + mt * C::BM);
+    k.rows = __builtin_amdgcn_readfirstlane(min(C::BM, nrows - mt * C::BM));
+    k.n0 = __builtin_amdgcn_readfirstlane(nt * COLS);
+    k.nst = __builtin_amdgcn_readfirstlane((second ? p1.Kd : p0.Kd) / SK_BKX);
+    return k;
+  };
+  auto prob = [&](const SkTile& k) -> const StreamProblem& { return k.p ? p1 : p0; };
+  // uniform base of weight block b of this wave for tile k
+  auto wbase = [&](const SkTile& k, int b) -> const char* {
+    const StreamProblem& P = prob(k);
+    const size_t gstride = static_cast<size_t>(P.Nd) * P.Kd;
+    const uint16_t* base;
+    int nb;
+    if (SWIGLU) {
+      base = (b < NBW / 2 ? P.w0 : P.w1) + k.g * gstride;
+      nb = k.n0 / 32 + w * (NBW / 2) + (b % (NBW / 2));
+    } else {
+      base = P.w0 + k.g * gstride;
+      nb = k.n0 / 32 + w * NBW + b;
+    }
+    return reinterpret_cast<const char*>(base + static_cast<size_t>(nb) * 32 * P.Kd);
+  };
+  // packed row (within the tile) behind this lane's DMA slot i
+  auto slot_row = [&](int i) -> int { return ((4 * i + w) * 64 + lane) >> 3; };
+  // direct-to-LDS copy of tile k's gathered activation rows into row buffer `slot`
+  // (rows past the tile repeat its last row)
+  auto fetch_rows = [&](const SkTile& k, int slot) {
+    const StreamProblem& P = prob(k);
+    if (P.row_index != nullptr) {
+      const int r = k.row0 + min(w * 64 + lane, k.rows - 1);
+      sk_dma4(static_cast<uint32_t>(r) * 4u, P.row_index, rows_base + slot * 1024 + w * 256);
+    }
+  };
+  // activation row of each of this lane's DMA slots for tile k
+  auto rows_of = [&](const SkTile& k, int slot, uint32_t* xr) {
+    const bool gathered = prob(k).row_index != nullptr;
+#pragma unroll
+    for (int i = 0; i < C::XDPW; ++i) {
+      const int r = min(slot_row(i), k.rows - 1);
+      xr[i] = static_cast<uint32_t>(gathered ? s_rows[slot][r] : k.row0 + r);
+    }
+  };
+  auto issue_x = [&](const SkTile& k, const uint32_t* xr, int ks, int ring_slot) {
+    const StreamProblem& P = prob(k);
+    const uint32_t kbytes = static_cast<uint32_t>(P.Kd) * 2u;
+    const uint32_t dst = lds_base + ring_slot * C::XSTAGE + w * 1024;
+#pragma unroll
+    for (int i = 0; i < C::XDPW; ++i) {
+      const int s = (4 * i + w) * 64 + lane;
+      const uint32_t off = xr[i] * kbytes +
+                           static_cast<uint32_t>(sk_swz(s >> 3, s & 7) * 16 + ks * (SK_BKX * 2));
+      sk_dma16(off, P.a, dst + i * 4096);
+    }
+  };
+
+  SkTile cur = tile_at(t);
+  bool has_n = t + step < t_end;
+  SkTile nxt = has_n ? tile_at(t + step) : cur;
+  const char* wc[NBW];
+  const char* wn[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    wc[b] = wbase(cur, b);
+    wn[b] = wbase(nxt, b);
+  }
+  int kslot = 0;  // row buffer of the current tile
+  fetch_rows(cur, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint32_t xc[C::XDPW];
+  rows_of(cur, 0, xc);
+
+  // prologue: the loads of virtual stages -V..-1, in the order a steady stage issues them
+  u32x4 wr[RS][SK_SPS][NBW];
+  constexpr int V = (SK_XS - 1) > RS ? (SK_XS - 1) : RS;
+  sk_unroll<V>([&](auto vc) {
+    constexpr int v = decltype(vc)::value - V;
+    constexpr int xs_t = v + SK_XS - 1;
+    if constexpr (xs_t >= 0) issue_x(cur, xc, xs_t, xs_t);
+    constexpr int ws_t = v + RS;
+    if constexpr (ws_t >= 0) {
+#pragma unroll
+      for (int u = 0; u < SK_SPS; ++u)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+          sk_ldg16(wr[ws_t][u][b], wc[b],
+                   static_cast<uint32_t>(((ws_t * SK_SPS + u) * 64 + lane) * 16));
+    }
+  });
+
+  int gs = 0;  // stages completed by this workgroup (activation ring position)
+  for (;;) {
+    fetch_rows(nxt, kslot ^ 1);  // published by the stage barriers before its first use
+    const bool has_nn = t + 2 * step < t_end;
+    const SkTile nn = has_nn ? tile_at(t + 2 * step) : nxt;
+    const int xb = __builtin_amdgcn_readfirstlane(ceil_div(cur.rows, 32));
+    const int nst = cur.nst;
+
+    floatx16 acc[NBW][XBM];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+      for (int j = 0; j < XBM; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][j][v] = 0.f;
+
+    for (int s0 = 0; s0 < nst; s0 += RS) {
+      sk_unroll<RS>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int s = s0 + r;
+        // this stage's weights and activations have landed in this wave's registers and
+        // LDS part; the barrier publishes the activations and retires every read of the
+        // slot that stage s + XS - 1 overwrites
+        wait_vmcnt<C::WAITN>();
+        __syncthreads();
+        {
+          const int ts = s + SK_XS - 1;
+          uint32_t xr[C::XDPW];
+          if (ts < nst) {
+#pragma unroll
+            for (int i = 0; i < C::XDPW; ++i) xr[i] = xc[i];
+            issue_x(cur, xr, ts, (gs + SK_XS - 1) % SK_XS);
+          } else {
+            rows_of(nxt, kslot ^ 1, xr);
+            issue_x(nxt, xr, ts - nst, (gs + SK_XS - 1) % SK_XS);
+          }
+        }
+        const char* xs = lds + (gs % SK_XS) * C::XSTAGE;
+        const int tw = s + RS;  // weight refill target stage (the next tile's past the end)
+        const bool w_in_cur = tw < nst;
+        const int kw = (w_in_cur ? tw : tw - nst) * SK_SPS;
+        auto xread = [&](int u, bf16x8* xv) {
+          const int kc = 2 * u + lh;
+#pragma unroll
+          for (int j = 0; j < XBM; ++j) {
+            const int row = 32 * j + lr;
+            xv[j] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(xs + row * (SK_BKX * 2) + (sk_swz(row, kc) << 4)));
+          }
+        };
+        bf16x8 xv[2][XBM];
+        xread(0, xv[0]);
+#pragma unroll
+        for (int u = 0; u < SK_SPS; ++u) {
+          const int cb = u & 1;
+          if (u + 1 < SK_SPS) xread(u + 1, xv[cb ^ 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < XBM; ++j) {
+            if (j >= xb) break;  // uniform: rows past the tile are never computed
+#pragma unroll
+            for (int b = 0; b < NBW; ++b)
+              acc[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, wr[r][u][b]), xv[cb][j], acc[b][j], 0, 0, 0);
+          }
+#pragma unroll
+          for (int b = 0; b < NBW; ++b)
+            sk_ldg16(wr[r][u][b], w_in_cur ? wc[b] : wn[b],
+                     static_cast<uint32_t>(((kw + u) * 64 + lane) * 16));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ++gs;
+      });
+    }
+
+    // epilogue: lane (lr, lh) holds row 32 j + lr, columns 8 q + 4 lh + {0..3} of each
+    // 32-wide block; one exchange between lane halves gives each lane two 16-byte pieces
+    // per row and block (columns 8 lh..+7 and 16 + 8 lh..+7)
+    {
+      const StreamProblem& P = prob(cur);
+      constexpr int OB = SWIGLU ? NBW / 2 : NBW;  // output blocks per wave
+#pragma unroll
+      for (int j = 0; j < XBM; ++j) {
+        if (j >= xb) break;
+        const int m = 32 * j + lr;
+        const bool ok = m < cur.rows;
+        uint16_t* orow = P.out + static_cast<size_t>(cur.row0 + (ok ? m : 0)) * P.Nd;
+#pragma unroll
+        for (int ob = 0; ob < OB; ++ob) {
+          u32x2 pk[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              h[e] = SWIGLU ? silu_f(acc[ob][j][4 * q + e]) * acc[ob + NBW / 2][j][4 * q + e]
+                            : acc[ob][j][4 * q + e];
+            pk[q] = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          }
+          // lh = 0 keeps q = 0, 2 and receives the partner's; lh = 1 keeps q = 1, 3
+          const u32x2 s0v = lh ? pk[0] : pk[1], s1v = lh ? pk[2] : pk[3];
+          u32x2 r0, r1;
+          r0[0] = __shfl_xor(s0v[0], 32, kWave);
+          r0[1] = __shfl_xor(s0v[1], 32, kWave);
+          r1[0] = __shfl_xor(s1v[0], 32, kWave);
+          r1[1] = __shfl_xor(s1v[1], 32, kWave);
+          const u32x4 ca = lh ? u32x4{r0[0], r0[1], pk[1][0], pk[1][1]}
+                              : u32x4{pk[0][0], pk[0][1], r0[0], r0[1]};
+          const u32x4 cb = lh ? u32x4{r1[0], r1[1], pk[3][0], pk[3][1]}
+                              : u32x4{pk[2][0], pk[2][1], r1[0], r1[1]};
+          const int n = cur.n0 + 32 * (SWIGLU ? w * (NBW / 2) + ob : w * NBW + ob);
+          if (ok) {
+            *reinterpret_cast<u32x4*>(orow + n + 8 * lh) = ca;
+            *reinterpret_cast<u32x4*>(orow + n + 16 + 8 * lh) = cb;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one block's values live at a time
+        }
+      }
+    }
+
+    if (!has_n) break;
+    cur = nxt;
+    nxt = nn;
+    has_n = has_nn;
+    t += step;
+    kslot ^= 1;
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      wc[b] = wn[b];
+      wn[b] = wbase(nxt, b);
+    }
+    rows_of(cur, kslot, xc);
+  }
+  wait_vmcnt<0>();  // no direct-to-LDS load may land after the workgroup ends
+}
+
+// tile shape: 2 weight blocks per wave, 128 rows, 4 stages of weights in flight
+constexpr int kNBW = 2, kXBM = 4, kRS = 4;
+
+bool fits(bool swiglu, const StreamProblem& P) {
+  if (P.rows <= 0) return true;
+  using C = SK<kNBW, kXBM, kRS>;
+  const int cols = swiglu ? C::COLS_SWIGLU : C::COLS_PLAIN;
+  const int nst = P.Kd / SK_BKX;
+  if (P.G <= 0 || P.G > kMaxN || P.a == nullptr || P.w0 == nullptr || P.out == nullptr)
+    return false;
+  if (swiglu && P.w1 == nullptr) return false;
+  if (P.Nd % cols != 0 || P.Kd % SK_BKX != 0 || nst % kRS != 0 || nst < kRS + SK_XS) return false;
+  // 32-bit byte offsets into the activations and the row index
+  const long a_rows = P.row_index != nullptr ? P.a_rows : P.rows;
+  if (a_rows <= 0 || a_rows * P.Kd * 2L >= (1L << 32)) return false;
+  if (P.rows * 4L >= (1L << 32)) return false;
+  return true;
+}
+
+}  // namespace
+
+bool stream_gemm_supported(bool swiglu, const StreamProblem& p0, const StreamProblem& p1) {
+  if (p0.rows <= 0 || !fits(swiglu, p0) || !fits(swiglu, p1)) return false;
+  if (p1.rows > 0 && (p1.offsets != nullptr || p1.G != 1 || p0.G + 1 > SK_THREADS)) return false;
+  return true;
+}
+
+hipError_t launch_stream_gemm(bool swiglu, const StreamProblem& p0, const StreamProblem& p1,
+                              hipStream_t stream) {
+  if (!stream_gemm_supported(swiglu, p0, p1)) return hipErrorNotSupported;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    cus[dev] = n;
+  }
+  const int grid = cus[dev] / 8 * 8;
+  if (grid <= 0) return hipErrorNotSupported;
+  if (swiglu)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, true>), dim3(grid), dim3(SK_THREADS),
+                       0, stream, p0, p1);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, false>), dim3(grid), dim3(SK_THREADS),
+                       0, stream, p0, p1);
+  return hipGetLastError();
+}

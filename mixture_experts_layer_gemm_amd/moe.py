@@ -54,8 +54,8 @@ def _load() -> ctypes.CDLL:
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
-        "moe_grouped_swiglu": (I, [I, I, I, I, I, P, P, P, I, P, P, P, P, P, P]),
-        "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, P, P, I, P, P, P, P]),
+        "moe_grouped_swiglu": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P]),
+        "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P]),
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
@@ -199,8 +199,8 @@ def moe_grouped_swiglu(a, offsets, w_gate, w_up, w_down, h=None, out=None, packe
     G, d_ff, _ = w_gate.shape
     h = torch.empty(rows, d_ff, dtype=a.dtype, device=a.device) if h is None else h
     out = torch.empty(rows, d, dtype=a.dtype, device=a.device) if out is None else out
-    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), int(packed), _ptr(a), _ptr(row_index),
-                                _ptr(offsets), rows,
+    st = lib.moe_grouped_swiglu(G, d, d_ff, _dt(a), int(packed), _ptr(a), a.shape[0],
+                                _ptr(row_index), _ptr(offsets), rows,
                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out),
                                 _stream())
     _check("moe_grouped_swiglu", st)
@@ -213,7 +213,7 @@ def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True, pac
     rows, Kd = _rows(a, row_index), a.shape[1]
     G, Nd, _ = w0.shape
     out = torch.empty(rows, Nd, dtype=a.dtype, device=a.device) if out is None else out
-    st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), int(packed), _ptr(a),
+    st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), int(packed), _ptr(a), a.shape[0],
                               _ptr(row_index), _ptr(offsets), rows, _ptr(w0), _ptr(w1), _ptr(out), _stream())
     _check("moe_grouped_gemm", st)
     return out

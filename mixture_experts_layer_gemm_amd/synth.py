@@ -111,6 +111,13 @@ SMALL = {
                      shared_widths=(64,), alpha=4.0, std_w=0.05),
     "S_N1": Config("small-one-expert", 18, T=77, d_model=64, N=1, K=1, d_r=64,
                    alpha=1.0, std_w=0.05),
+    # shapes of the persistent GEMM (widths multiples of 256, >= 512), with more tiles
+    # than compute units so that tiles follow one another in a workgroup
+    "S_stream": Config("small-stream", 19, T=2048, d_model=1024, N=8, K=4, d_r=1024,
+                       shared_widths=(512,), alpha=4.0, std_w=0.03),
+    "S_stream_cap": Config("small-stream-capacity-gate", 20, T=2048, d_model=512, N=16, K=4,
+                           d_r=512, shared_widths=(256, 256), renorm=False, alpha=1.0,
+                           capacity_factor=1.0, zipf_bias=True, shared_gate=True, std_w=0.04),
 }
 
 

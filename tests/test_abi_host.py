@@ -93,11 +93,13 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, None, 0, None) == \
         moe.MOE_ERR_WORKSPACE
     assert L.moe_permute(0, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, None, 0, None) == moe.MOE_OK
-    assert L.moe_grouped_swiglu(2, 64, 100, 1, 0, 1, None, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_grouped_swiglu(2, 64, 128, 1, 0, 1, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_grouped_swiglu(1, 64, 128, 1, 0, 1, None, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
-    assert L.moe_grouped_swiglu(1, 64, 128, 0, 1, 1, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 2, 1, None, None, 8, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_swiglu(2, 64, 100, 1, 0, 1, 0, None, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_swiglu(2, 64, 128, 1, 0, 1, 0, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_swiglu(1, 64, 128, 1, 0, 1, 0, None, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
+    assert L.moe_grouped_swiglu(1, 64, 128, 0, 1, 1, 0, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 2, 1, 0, None, None, 8, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 1, 1, 0, 1, None, 8, 1, 1, 1, None) == \
+        moe.MOE_ERR_INVALID_ARG                               # row index needs a_rows
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
     assert L.moe_pack_weights(2, 96, 128, 1, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # N % 64
     assert L.moe_pack_weights(2, 64, 128, 1, 4096, 4096 + 100, None) == moe.MOE_ERR_INVALID_ARG  # overlap

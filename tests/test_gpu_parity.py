@@ -29,7 +29,7 @@ def setup_module(module):
 
 
 SMALL = ["C0", "S_softmax", "S_sigmoid", "S_selected", "S_capgate", "S_cap3shared", "S_f32",
-         "S_tied", "S_KeqN", "S_N1"]
+         "S_tied", "S_KeqN", "S_N1", "S_stream", "S_stream_cap"]
 _cache = {}
 
 
@@ -196,6 +196,42 @@ def test_grouped_swiglu_gathered_rows(dtype, packed):
         H, F = O.swiglu(dec(a_s[row_index[lo:hi]]), dec(wg_s[g]), dec(wu_s[g]), dec(wd_s[g]))
         assert_close(h[lo:hi], H, dtype, f"H segment {g}")
         assert_close(out[lo:hi], F, dtype, f"F segment {g}")
+
+
+@pytest.mark.parametrize("gathered", [False, True])
+def test_grouped_swiglu_persistent_shapes(gathered):
+    """Shapes of the persistent GEMM (d_model, d_ff multiples of 256): ragged groups
+    (empty, one row, many 128-row tiles) and more tiles than compute units, so that each
+    workgroup runs several tiles back to back; optionally gathered rows."""
+    say(f"grouped swiglu, persistent-kernel shapes, gathered={gathered}")
+    rng = np.random.default_rng(29 + gathered)
+    seg = [0, 1, 129, 0, 1000, 31, 256, 257, 700, 300, 640, 5, 900, 128, 511, 2]
+    G, d, dff = len(seg), 768, 1024
+    rows = sum(seg)
+    offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int32)
+
+    def draw(shape, std):
+        return synth.bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+    n_src = 3000 if gathered else rows
+    a_s = draw((n_src, d), 1.0)
+    ri = rng.integers(0, n_src, size=rows).astype(np.int32) if gathered else None
+    wg_s, wu_s, wd_s = draw((G, dff, d), 0.03), draw((G, dff, d), 0.03), draw((G, d, dff), 0.03)
+    dec = synth.bf16_to_f32
+    wg_d, wu_d, wd_d = (moe.moe_pack_weights(to_device(w, "bf16")) for w in (wg_s, wu_s, wd_s))
+    h, out = moe.moe_grouped_swiglu(to_device(a_s, "bf16"), torch.from_numpy(offsets).cuda(),
+                                    wg_d, wu_d, wd_d, packed=True,
+                                    row_index=None if ri is None else torch.from_numpy(ri).cuda())
+    torch.cuda.synchronize()
+    h, out = host(h), host(out)
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi == lo:
+            continue
+        src = a_s[ri[lo:hi]] if gathered else a_s[lo:hi]
+        H, F = O.swiglu(dec(src), dec(wg_s[g]), dec(wu_s[g]), dec(wd_s[g]))
+        assert_close(h[lo:hi], H, "bf16", f"H segment {g}")
+        assert_close(out[lo:hi], F, "bf16", f"F segment {g}")
 
 
 # ---------------------------------------------------------------------------------------
