@@ -3,11 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C1]
 
-A step is one whole-layer forward (router -> permute -> grouped SwiGLU experts -> shared
-MLP -> combine) over one batch of seeded synthetic tokens resident in HBM. Prints one
-JSON line: whole-layer tokens/s, the grouped-GEMM TFLOP/s, the roofline of the dominant
-kernel (the routed gate/up grouped GEMM with fused SwiGLU), per-stage times and the
-CPU oracle timed on a bounded sample of the same workload.
+A step is one whole-layer forward (router -> permute -> grouped SwiGLU experts and the
+shared MLP -> combine) over one batch of seeded synthetic tokens resident in HBM. Prints
+one JSON line: whole-layer tokens/s, the expert-GEMM TFLOP/s, the roofline of the
+dominant kernel (the gate/up pass: routed experts with gathered rows plus the shared
+MLP, one persistent launch, SwiGLU fused), per-stage times and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -26,8 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 64e K=4"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_gemm_amd", "csrc", "gemm_packed.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_olmo64e_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_gemm_amd", "csrc", "gemm_stream.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "experts_gateup_olmo64e_traffic.json")
 
 
 def log(*a):
@@ -177,24 +178,24 @@ def main():
     R = int(o["offsets"][-1].item())
     esz = 2 if dt == "bf16" else 4
     rows = layer.rows
-    h_perm, f_perm = o["h_perm"], o["f_perm"]
     reps = args.stage_reps
     log("stage timings")
     st = {}
     pk = layer.weights_packed
     lw = layer.tensors                 # the layer's own (packed) weights
-    # the gate/up pass gathers its rows from x through row_token, as in moe_forward
-    st["gemm_gateup_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
-        x, o["offsets"], lw["w_gate"], lw["w_up"], out=h_perm, swiglu=True, packed=pk,
-        row_index=o["row_token"]), reps)
-    st["gemm_down_ms"] = time_eager(torch, lambda: moe.moe_grouped_gemm(
-        h_perm, o["offsets"], lw["w_down"], out=f_perm, swiglu=False, packed=pk), reps)
     sm = layer.shared_mlp
-    if sm is not None:
-        hs = torch.empty(T, sm[0].shape[0], dtype=x.dtype, device=x.device)
-        g_out = torch.empty(T, d, dtype=x.dtype, device=x.device)
-        st["shared_mlp_ms"] = time_eager(torch, lambda: moe.moe_grouped_swiglu(
-            x, None, sm[0][None], sm[1][None], sm[2][None], h=hs, out=g_out, packed=pk), reps)
+    d_s = 0 if sm is None else sm[0].shape[0]
+    bufs = dict(h_perm=o["h_perm"], f_perm=o["f_perm"],
+                h_shared=torch.empty(T, d_s, dtype=x.dtype, device=x.device) if d_s else None,
+                g=torch.empty(T, d, dtype=x.dtype, device=x.device) if d_s else None)
+
+    def experts(pass_):
+        return lambda: moe.moe_experts(x, o["row_token"], o["offsets"], rows, lw["w_gate"],
+                                       lw["w_up"], lw["w_down"], shared=sm, out=bufs,
+                                       packed=pk, pass_=pass_)
+    # the dominant kernel: the gate/up pass, timed with events on its own stream
+    st["experts_gateup_ms"] = time_eager(torch, experts(1), reps)
+    st["experts_down_ms"] = time_eager(torch, experts(2), reps)
     logits = torch.empty(T, N, dtype=torch.float32, device=x.device)
     st["route_ms"] = time_graph(torch, lambda: moe.moe_route(
         x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
@@ -204,20 +205,32 @@ def main():
                                   reps)
     y2 = torch.empty_like(layer.y)
     st["combine_ms"] = time_graph(torch, lambda: moe.moe_combine(
-        f_perm, o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2), reps)
+        o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
+        reps)
 
-    flops_gateup = 4.0 * R * d * d_r
-    flops_down = 2.0 * R * d * d_r
+    # algorithmic work (each counted once): flops of the contractions; bytes = weights of
+    # the active experts and the shared MLP, x read once, h written once
     act_experts = int((o["C_keep"] > 0).sum().item())
-    bytes_gateup = 2 * act_experts * d_r * d * esz + R * d * esz + R * d_r * esz
-    gemm_tflops = (flops_gateup + flops_down) / ((st["gemm_gateup_ms"] + st["gemm_down_ms"]) * 1e-3) / 1e12
-    achieved = flops_gateup / (st["gemm_gateup_ms"] * 1e-3) / 1e12
-    traffic = measured_traffic()
+    flops_gateup = 4.0 * R * d * d_r + 4.0 * T * d * d_s
+    flops_experts = 6.0 * R * d * d_r + 6.0 * T * d * d_s
+    bytes_gateup = esz * (2 * act_experts * d_r * d + 2 * d_s * d + T * d + R * d_r + T * d_s)
+    t_gateup = st["experts_gateup_ms"] * 1e-3
+    expert_tflops = flops_experts / ((st["experts_gateup_ms"] + st["experts_down_ms"]) * 1e-3) / 1e12
+    t_mfma = flops_gateup / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = bytes_gateup / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:   # the binding roofline of this shape
+        roof = {"bound": "hbm", "achieved": round(bytes_gateup / t_gateup / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops_gateup / t_gateup / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic()
     hbm = {
         "route": (T * d * esz + N * d * esz + T * K * 8) / (st["route_ms"] * 1e-3) / 1e9,
         # count: idx in, ranks out; map: idx + ranks in, dest_row + row_token out
         "permute": (T * K * 20 + R * 4) / (st["permute_ms"] * 1e-3) / 1e9,
-        "combine": (R * d * esz + (2 if layer.shared_mlp is not None else 1) * T * d * esz + T * K * 8)
+        "combine": (R * d * esz + (2 if d_s else 1) * T * d * esz + T * K * 8)
         / (st["combine_ms"] * 1e-3) / 1e9,
     }
     out = {
@@ -238,14 +251,14 @@ def main():
                    "score": ["softmax", "sigmoid", "softmax_selected"][cfg.score],
                    "renorm": cfg.renorm, "alpha": cfg.alpha, "capacity": cap,
                    "kept_routes": R, "active_experts": act_experts},
-        "grouped_gemm_tflops": round(gemm_tflops, 1),
-        "grouped_gemm_frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"kernel": "routed gate/up grouped GEMM + fused SwiGLU (gemm_packed_kernel<true,true>)"
-                     if pk else "routed gate/up grouped GEMM + fused SwiGLU (gemm_bf16_kernel<true,true>)",
-                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": bytes_gateup,
-                     "flops_per_launch": flops_gateup},
+        "expert_gemm_tflops": round(expert_tflops, 1),
+        "expert_gemm_frac_bf16_peak": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": dict(kernel="gate/up pass: routed experts (gathered rows) + shared MLP, "
+                         "SwiGLU fused (gemm_stream_kernel<2,4,4,true>)" if pk else
+                         "routed gate/up grouped GEMM (row-major weights)",
+                         **roof, algorithmic_bytes=bytes_gateup, flops_per_launch=flops_gateup,
+                         mfma_tflops=round(flops_gateup / t_gateup / 1e12, 1),
+                         mfma_frac=round(flops_gateup / t_gateup / 1e12 / PEAK_BF16_TFLOPS, 4)),
         "stages_ms": {k.replace("_ms", ""): round(v, 4) for k, v in st.items()},
         "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
     }

@@ -199,6 +199,35 @@ int moe_pack_weights(int G, int N_dim, int K_dim, int dt, const void* w, void* w
                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_experts: the expert stage of the layer, the routed experts over their real-count
+ * segments together with the shared MLP (Section 20 Eq. 74-76 over the offsets of
+ * Section 10 Eq. 26), as moe_forward runs it:
+ *   routed, rows r of expert i in [offsets[i], offsets[i+1]), t = row_token[r]:
+ *     h_perm[r] = SiLU(x[t] W_g,i^T) * (x[t] W_u,i^T),   f_perm[r] = h_perm[r] W_d,i^T
+ *   shared (d_s > 0), every token t:
+ *     h_shared[t] = SiLU(x[t] Ws_g^T) * (x[t] Ws_u^T),     g[t] = h_shared[t] Ws_d^T
+ * With packed weights and widths that the persistent kernel takes (bf16; d_model and d_s
+ * multiples of 256, >= 512; d_r a multiple of 256, >= 512) each pass is ONE launch that
+ * holds both problems; otherwise the passes run as separate grouped GEMMs.
+ *
+ *   N, d_model, d_r    routed experts and widths; w_gate, w_up [N][d_r][d_model],
+ *                      w_down [N][d_model][d_r]
+ *   d_s                shared MLP width (0 = none); ws_gate, ws_up [d_s][d_model],
+ *                      ws_down [d_model][d_s] (NULL when d_s == 0)
+ *   packed             weights in the moe_pack_weights layout (1) or row-major (0)
+ *   x                  [T][d_model]
+ *   row_token, offsets moe_permute's restoration map and offsets ([max_rows], [N+1])
+ *   h_perm, f_perm     [max_rows][d_r], [max_rows][d_model] out
+ *   h_shared, g        [T][d_s], [T][d_model] out
+ *   pass               1: gate/up only, 2: down only (reads h_perm, h_shared), 0: both
+ * ------------------------------------------------------------------------------- */
+int moe_experts(int N, int d_model, int d_r, int d_s, int dt, int packed, const void* x, int T,
+                const int32_t* row_token, const int32_t* offsets, int max_rows,
+                const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                const void* ws_up, const void* ws_down, void* h_perm, void* f_perm,
+                void* h_shared, void* g, int pass, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_combine: y[t] = sum_{k : dest_row[t][k] >= 0} r[t][k] f_perm[dest_row[t][k]]
  *                     + s_t g[t]                                   (Section 21 Eq. 80)
  * Dropped routes contribute nothing and the kept coefficients are not renormalized

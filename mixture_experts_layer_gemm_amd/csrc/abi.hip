@@ -233,6 +233,52 @@ static hipError_t gemm_pass(bool swiglu, bool packed, int G, int Kd, int Nd, int
                              stream);
 }
 
+// The routed experts over their segments (rows gathered from x through row_token) and
+// the shared MLP over all T tokens: pass 1 = gate/up, 2 = down, 0 = both. With packed
+// weights and shapes that fit, each pass is one persistent launch holding both problems.
+static hipError_t expert_passes(int N, int d, int d_r, int d_s, int dt, bool pk, const void* x,
+                                int T, const int32_t* row_token, const int32_t* offsets,
+                                int rows, const void* w_gate, const void* w_up,
+                                const void* w_down, const void* ws_gate, const void* ws_up,
+                                const void* ws_down, void* h_perm, void* f_perm, void* h_shared,
+                                void* g, int pass, hipStream_t stream) {
+  const bool up = pass != 2, down = pass != 1;
+  if (pk && rows > 0 && d_s > 0) {
+    const StreamProblem gu0 = problem(x, T, row_token, offsets, N, rows, d, d_r, w_gate, w_up, h_perm);
+    const StreamProblem gu1 = problem(x, T, nullptr, nullptr, 1, T, d, d_s, ws_gate, ws_up, h_shared);
+    const StreamProblem dn0 = problem(h_perm, rows, nullptr, offsets, N, rows, d_r, d, w_down,
+                                      nullptr, f_perm);
+    const StreamProblem dn1 = problem(h_shared, T, nullptr, nullptr, 1, T, d_s, d, ws_down,
+                                      nullptr, g);
+    if (stream_gemm_supported(true, gu0, gu1) && stream_gemm_supported(false, dn0, dn1)) {
+      if (up) {
+        const hipError_t e = launch_stream_gemm(true, gu0, gu1, stream);
+        if (e != hipSuccess) return e;
+      }
+      if (down) return launch_stream_gemm(false, dn0, dn1, stream);
+      return hipSuccess;
+    }
+  }
+  hipError_t e = hipSuccess;
+  if (rows > 0) {
+    if (up)
+      e = gemm_pass(true, pk, N, d, d_r, dt, x, T, row_token, offsets, rows, w_gate, w_up,
+                    h_perm, stream);
+    if (e == hipSuccess && down)
+      e = gemm_pass(false, pk, N, d_r, d, dt, h_perm, rows, nullptr, offsets, rows, w_down,
+                    nullptr, f_perm, stream);
+  }
+  if (e == hipSuccess && d_s > 0) {
+    if (up)
+      e = gemm_pass(true, pk, 1, d, d_s, dt, x, T, nullptr, nullptr, T, ws_gate, ws_up, h_shared,
+                    stream);
+    if (e == hipSuccess && down)
+      e = gemm_pass(false, pk, 1, d_s, d, dt, h_shared, T, nullptr, nullptr, T, ws_down, nullptr,
+                    g, stream);
+  }
+  return e;
+}
+
 int moe_grouped_swiglu(int G, int d_model, int d_ff, int dt, int packed, const void* a,
                        int a_rows, const int32_t* row_index, const int32_t* offsets,
                        int max_rows, const void* w_gate,
@@ -286,6 +332,31 @@ int moe_grouped_gemm(int G, int K_dim, int N_dim, int dt, int swiglu, int packed
   return MOE_OK;
 }
 
+int moe_experts(int N, int d_model, int d_r, int d_s, int dt, int packed, const void* x, int T,
+                const int32_t* row_token, const int32_t* offsets, int max_rows,
+                const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                const void* ws_up, const void* ws_down, void* h_perm, void* f_perm,
+                void* h_shared, void* g, int pass, hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (packed != 0 && packed != 1) return MOE_ERR_INVALID_ARG;
+  if (packed && dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (pass < 0 || pass > 2) return MOE_ERR_INVALID_ARG;
+  if (N <= 0 || d_model <= 0 || d_r <= 0 || d_s < 0 || T < 0 || max_rows < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (N > moe::kMaxN || d_model % 64 != 0 || d_r % 64 != 0 || d_s % 64 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  if (max_rows > 0 && (!x || !row_token || !offsets || !w_gate || !w_up || !w_down || !h_perm ||
+                       !f_perm || T <= 0))
+    return MOE_ERR_INVALID_ARG;
+  if (d_s > 0 && (!x || !ws_gate || !ws_up || !ws_down || !h_shared || !g))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  MOE_HIP(expert_passes(N, d_model, d_r, d_s, dt, packed == 1, x, T, row_token, offsets, max_rows,
+                        w_gate, w_up, w_down, ws_gate, ws_up, ws_down, h_perm, f_perm, h_shared,
+                        g, pass, stream));
+  return MOE_OK;
+}
+
 int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
                 const int32_t* dest_row, const float* topk_r, const void* g, float s,
                 const float* s_tok, void* y, hipStream_t stream) {
@@ -330,39 +401,9 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   MOE_HIP(launch_scan(T, N, a->capacity, w.hist, w.C_req, w.C_keep, w.offsets, stream));
   MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
-  const bool pk = a->weights_packed == 1;
-  // routed experts (p0) and the shared MLP (p1) in one persistent launch per pass when
-  // the shapes fit it
-  bool fused = false;
-  if (pk && rows > 0 && a->d_s > 0) {
-    const StreamProblem gu0 = problem(a->x, T, w.row_token, w.offsets, N, rows, d, a->d_r,
-                                      a->w_gate, a->w_up, w.h_perm);
-    const StreamProblem gu1 = problem(a->x, T, nullptr, nullptr, 1, T, d, a->d_s, a->ws_gate,
-                                      a->ws_up, w.h_shared);
-    const StreamProblem dn0 = problem(w.h_perm, rows, nullptr, w.offsets, N, rows, a->d_r, d,
-                                      a->w_down, nullptr, w.f_perm);
-    const StreamProblem dn1 = problem(w.h_shared, T, nullptr, nullptr, 1, T, a->d_s, d,
-                                      a->ws_down, nullptr, w.g);
-    if (stream_gemm_supported(true, gu0, gu1) && stream_gemm_supported(false, dn0, dn1)) {
-      MOE_HIP(launch_stream_gemm(true, gu0, gu1, stream));
-      MOE_HIP(launch_stream_gemm(false, dn0, dn1, stream));
-      fused = true;
-    }
-  }
-  if (!fused) {
-    if (rows > 0) {
-      MOE_HIP(gemm_pass(true, pk, N, d, a->d_r, a->dt, a->x, T, w.row_token, w.offsets, rows,
-                        a->w_gate, a->w_up, w.h_perm, stream));
-      MOE_HIP(gemm_pass(false, pk, N, a->d_r, d, a->dt, w.h_perm, rows, nullptr, w.offsets,
-                        rows, a->w_down, nullptr, w.f_perm, stream));
-    }
-    if (a->d_s > 0) {
-      MOE_HIP(gemm_pass(true, pk, 1, d, a->d_s, a->dt, a->x, T, nullptr, nullptr, T, a->ws_gate,
-                        a->ws_up, w.h_shared, stream));
-      MOE_HIP(gemm_pass(false, pk, 1, a->d_s, d, a->dt, w.h_shared, T, nullptr, nullptr, T,
-                        a->ws_down, nullptr, w.g, stream));
-    }
-  }
+  MOE_HIP(expert_passes(N, d, a->d_r, a->d_s, a->dt, a->weights_packed == 1, a->x, T,
+                        w.row_token, w.offsets, rows, a->w_gate, a->w_up, a->w_down, a->ws_gate,
+                        a->ws_up, a->ws_down, w.h_perm, w.f_perm, w.h_shared, w.g, 0, stream));
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));
   return MOE_OK;

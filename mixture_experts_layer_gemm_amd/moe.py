@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P]),
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
+        "moe_experts": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, I, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
         "moe_forward": (I, [POINTER(ForwardArgs), P, S, P]),
     }
@@ -216,6 +217,32 @@ def moe_grouped_gemm(a, offsets, w0, w1=None, out=None, swiglu: bool = True, pac
     st = lib.moe_grouped_gemm(G, Kd, Nd, _dt(a), int(swiglu), int(packed), _ptr(a), a.shape[0],
                               _ptr(row_index), _ptr(offsets), rows, _ptr(w0), _ptr(w1), _ptr(out), _stream())
     _check("moe_grouped_gemm", st)
+    return out
+
+
+def moe_experts(x, row_token, offsets, max_rows: int, w_gate, w_up, w_down, shared=None,
+                out=None, packed=False, pass_: int = 0):
+    """The expert stage as moe_forward runs it: routed experts over their segments (rows
+    gathered from x through row_token) and the shared MLP `shared` = (ws_gate, ws_up,
+    ws_down) or None. Returns dict(h_perm, f_perm, h_shared, g); pass_ 1 = gate/up only,
+    2 = down only (reusing the h buffers of `out`), 0 = both."""
+    T, d = x.shape
+    N, d_r, _ = w_gate.shape
+    d_s = 0 if shared is None else shared[0].shape[0]
+    dev, dt = x.device, x.dtype
+    if out is None:
+        rows = max(max_rows, 1)
+        out = dict(h_perm=torch.empty(rows, d_r, dtype=dt, device=dev),
+                   f_perm=torch.empty(rows, d, dtype=dt, device=dev),
+                   h_shared=torch.empty(T, d_s, dtype=dt, device=dev) if d_s else None,
+                   g=torch.empty(T, d, dtype=dt, device=dev) if d_s else None)
+    ws = (None, None, None) if shared is None else shared
+    st = lib.moe_experts(N, d, d_r, d_s, _dt(x), int(packed), _ptr(x), T, _ptr(row_token),
+                         _ptr(offsets), max_rows, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                         _ptr(ws[0]), _ptr(ws[1]), _ptr(ws[2]), _ptr(out["h_perm"]),
+                         _ptr(out["f_perm"]), _ptr(out["h_shared"]), _ptr(out["g"]), pass_,
+                         _stream())
+    _check("moe_experts", st)
     return out
 
 

@@ -9,7 +9,8 @@ from mixture_experts_layer_gemm_amd import moe
 from mixture_experts_layer_gemm_amd import synth
 import oracle.moe_oracle as O
 
-EXPECTED = ["moe_capacity_from_factor", "moe_combine", "moe_forward", "moe_forward_workspace_size",
+EXPECTED = ["moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
+            "moe_forward_workspace_size",
             "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_pack_weights", "moe_permute",
             "moe_permute_workspace_size",
             "moe_route", "moe_route_workspace_size", "moe_status_string"]
@@ -101,6 +102,13 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 1, 1, 0, 1, None, 8, 1, 1, 1, None) == \
         moe.MOE_ERR_INVALID_ARG                               # row index needs a_rows
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
+    ex = [8, 512, 512, 512, 1, 1, 1, 64, 1, 1, 64, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1]
+    assert L.moe_experts(*ex, 3, None) == moe.MOE_ERR_INVALID_ARG          # pass out of range
+    assert L.moe_experts(*ex[:5], 2, *ex[6:], 0, None) == moe.MOE_ERR_INVALID_ARG  # packed 0/1
+    bad = list(ex)
+    bad[12] = None                                                          # no w_gate
+    assert L.moe_experts(*bad, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_experts(*ex[:7], 0, 1, 1, 0, *ex[11:], 0, None) == moe.MOE_OK  # T = 0
     assert L.moe_pack_weights(2, 96, 128, 1, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # N % 64
     assert L.moe_pack_weights(2, 64, 128, 1, 4096, 4096 + 100, None) == moe.MOE_ERR_INVALID_ARG  # overlap
     assert L.moe_combine(4, 64, 17, 1, 1, 1, 1, None, 1.0, None, 1, None) == moe.MOE_ERR_UNSUPPORTED

@@ -234,6 +234,49 @@ def test_grouped_swiglu_persistent_shapes(gathered):
         assert_close(out[lo:hi], F, "bf16", f"F segment {g}")
 
 
+@pytest.mark.parametrize("name", ["S_stream", "S_stream_cap", "S_softmax"])
+def test_expert_stage(name):
+    """moe_experts (routed experts + shared MLP; one launch per pass when the shapes fit
+    the persistent kernel, else separate grouped GEMMs): the gate/up and down passes run
+    separately give the same bits as both at once, and the outputs match the oracle."""
+    L = layer(name)
+    c = L.cfg
+    say(f"expert stage {name}")
+    inp = L.inp
+    z = O.router_logits(L.x_f(), inp.as_float(inp.w_router), inp.logit_bias)
+    idx = O.topk_select(z, c.K)
+    pm = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity, copy_rows=False)
+    perm = O.permutation(idx, O.keep_routes(idx, c.N, L.capacity), c.N)
+    rows = moe.max_rows(L.T, c.N, c.K, L.capacity)
+    wg, wu, wd = (moe.moe_pack_weights(w) for w in (L.w_gate, L.w_up, L.w_down))
+    sm = moe.pack_shared(L.shared) if L.shared else None
+    if sm is not None:
+        sm = tuple(moe.moe_pack_weights(w[None])[0] for w in sm)
+    both = moe.moe_experts(L.x, pm["row_token"], pm["offsets"], rows, wg, wu, wd, shared=sm,
+                           packed=True)
+    split = moe.moe_experts(L.x, pm["row_token"], pm["offsets"], rows, wg, wu, wd, shared=sm,
+                            packed=True, pass_=1)
+    moe.moe_experts(L.x, pm["row_token"], pm["offsets"], rows, wg, wu, wd, shared=sm,
+                    packed=True, pass_=2, out=split)
+    torch.cuda.synchronize()
+    R = int(perm.offsets[-1])
+    for k in ("h_perm", "f_perm", "h_shared", "g"):
+        if both[k] is None:
+            continue
+        n = R if k in ("h_perm", "f_perm") else L.T
+        assert torch.equal(both[k][:n].view(torch.int16), split[k][:n].view(torch.int16)), k
+    Hg, Fg = host(both["h_perm"])[:R], host(both["f_perm"])[:R]
+    xs = L.x_f()
+    for e in range(c.N):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi > lo:
+            H, F = O.swiglu(xs[perm.row_token[lo:hi]], *inp.expert_f32(e))
+            assert_close(Hg[lo:hi], H, "bf16", f"H expert {e}")
+            assert_close(Fg[lo:hi], F, "bf16", f"F expert {e}")
+    if sm is not None:
+        assert_close(host(both["g"]), O.shared_output(xs, inp.shared_f32()), "bf16", "G")
+
+
 # ---------------------------------------------------------------------------------------
 # a8: combine
 # ---------------------------------------------------------------------------------------
