@@ -10,10 +10,11 @@
 // (the shared MLP over all tokens), so the shared expert fills the routed pass's tail.
 //
 // Schedule (one workgroup of 4 waves per compute unit):
-//   * tiles are ordered (problem, group, n-tile, m-tile); the 8 contiguous eighths of
-//     that list go to the 8 XCDs (workgroup b runs on XCD b % 8) and the workgroups of
-//     an XCD take every (grid / 8)-th tile of its eighth, so the row tiles that share a
-//     weight block run at the same time behind the same L2;
+//   * tiles are ordered (problem, group, n-tile, m-tile); 8 contiguous parts of that list
+//     of equal cost (active 32-row blocks x k stages) go to the 8 XCDs (workgroup b runs
+//     on XCD b % 8) and the workgroups of an XCD take every (grid / 8)-th tile of its
+//     part, so the row tiles that share a weight block run at the same time behind the
+//     same L2;
 //   * every wave streams its NBW weight blocks straight into registers, RS stages
 //     (64 k each) ahead, in a register ring; activations go through a 4-stage LDS ring
 //     filled by direct-to-LDS loads; in the last stages of a tile both rings are already
@@ -109,6 +110,7 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   constexpr int COLS = SWIGLU ? C::COLS_SWIGLU : C::COLS_PLAIN;
   __shared__ int s_off[kMaxN + 2];     // packed row offsets of the groups (p1 last)
   __shared__ int s_tstart[SK_THREADS + 1];
+  __shared__ int s_cstart[SK_THREADS + 1];
   __shared__ int s_rows[2][256];       // gathered activation rows of the current / next tile
   __shared__ __attribute__((aligned(1024))) char lds[SK_XS * C::XSTAGE];
   typedef __attribute__((address_space(3))) char lds_char;
@@ -116,32 +118,69 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   const int G0 = p0.G;
   const int NG = G0 + (p1.rows > 0 ? 1 : 0);  // groups over both problems (<= 256)
 
-  // ---- tile list: per-group tile counts, prefix-summed in LDS ----
+  // ---- tile list: per-group tile counts and costs, prefix-summed in LDS ----
+  // cost of a tile = active 32-row blocks x k stages; a group's tiles cost
+  // n-tiles x ceil(rows / 32) x stages in all
   for (int g = tid; g <= G0; g += SK_THREADS)
     s_off[g] = (p0.offsets != nullptr) ? p0.offsets[g] : (g == 0 ? 0 : p0.rows);
   __syncthreads();
   if (tid == 0) s_off[G0 + 1] = s_off[G0] + p1.rows;
   __syncthreads();
   {
-    int cnt = 0;
-    if (tid < G0) cnt = ceil_div(s_off[tid + 1] - s_off[tid], C::BM) * (p0.Nd / COLS);
-    else if (tid == G0 && NG > G0) cnt = ceil_div(p1.rows, C::BM) * (p1.Nd / COLS);
+    int cnt = 0, cost = 0;
+    if (tid < NG) {
+      const StreamProblem& P = tid < G0 ? p0 : p1;
+      const int nrows = s_off[tid + 1] - s_off[tid];
+      cnt = ceil_div(nrows, C::BM) * (P.Nd / COLS);
+      cost = (P.Nd / COLS) * ceil_div(nrows, 32) * (P.Kd / SK_BKX);
+    }
     s_tstart[tid + 1] = cnt;
+    s_cstart[tid + 1] = cost;
   }
-  if (tid == 0) s_tstart[0] = 0;
+  if (tid == 0) {
+    s_tstart[0] = 0;
+    s_cstart[0] = 0;
+  }
   __syncthreads();
-  for (int off = 1; off < SK_THREADS; off <<= 1) {  // inclusive scan over <= 256 groups
+  for (int off = 1; off < SK_THREADS; off <<= 1) {  // inclusive scans over <= 256 groups
     const int v = (tid >= off) ? s_tstart[tid + 1 - off] : 0;
+    const int c = (tid >= off) ? s_cstart[tid + 1 - off] : 0;
     __syncthreads();
     s_tstart[tid + 1] += v;
+    s_cstart[tid + 1] += c;
     __syncthreads();
   }
   const int total = s_tstart[NG];
+  // this XCD's contiguous share of the tile list: from the first tile whose cost prefix
+  // reaches xcd / 8 of the total cost to the first that reaches (xcd + 1) / 8
+  auto first_tile_at_cost = [&](long target) -> int {
+    if (target <= 0) return 0;
+    if (target >= s_cstart[NG]) return total;
+    int lo = 0, hi = NG - 1;  // group with s_cstart[g] < target <= s_cstart[g + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cstart[mid + 1] < target) lo = mid + 1; else hi = mid;
+    }
+    const StreamProblem& P = lo < G0 ? p0 : p1;
+    const int nrows = s_off[lo + 1] - s_off[lo];
+    const int rb = ceil_div(nrows, 32), mtiles = ceil_div(nrows, C::BM);
+    const int nst = P.Kd / SK_BKX;
+    const long u = (target - s_cstart[lo] + nst - 1) / nst;  // 32-row blocks into the group
+    int nt = static_cast<int>(u / rb);
+    const int rem = static_cast<int>(u - static_cast<long>(nt) * rb);
+    int mt = ceil_div(rem, XBM);
+    if (mt >= mtiles) {
+      ++nt;
+      mt = 0;
+    }
+    return min(total, s_tstart[lo] + nt * mtiles + mt);
+  };
   const int step = gridDim.x >> 3;
-  const int seg = ceil_div(total, 8);
   const int xcd = blockIdx.x & 7;
-  const int t_end = min(total, (xcd + 1) * seg);
-  int t = xcd * seg + (blockIdx.x >> 3);
+  const long ctot = s_cstart[NG];
+  const int t_beg = __builtin_amdgcn_readfirstlane(first_tile_at_cost(ctot * xcd / 8));
+  const int t_end = __builtin_amdgcn_readfirstlane(first_tile_at_cost(ctot * (xcd + 1) / 8));
+  int t = t_beg + (blockIdx.x >> 3);
   if (t >= t_end) return;
 
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
