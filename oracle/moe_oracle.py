@@ -190,6 +190,102 @@ def permutation(idx, kept, N: int) -> Permutation:
 
 
 # ----------------------------------------------------------------------------------------
+# f1: router balance statistics and drop diagnostics (forward values, no gradients)
+# ----------------------------------------------------------------------------------------
+def normalized_scores(z, score: int) -> np.ndarray:
+    """p_{t,i}: each token's router scores normalized across all N experts (p5 Eq. 38).
+    Softmax routing: the full softmax of the (biased) logits, whatever the combine rule;
+    sigmoid routing: the affinities divided by their sum over the experts (p5 Section
+    10.7, the scores of the balance loss are normalized across experts)."""
+    z = _f64(z)
+    if score == SIGMOID:
+        a = _sigmoid(z)
+        return a / a.sum(axis=1, keepdims=True)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def imbalance_max(x) -> float:
+    """Max/mean imbalance n * max_j x_j / sum_j x_j of a load vector (p5 Eq. 22, Eq. 39);
+    NaN for an all-zero vector."""
+    x = _f64(x)
+    tot = x.sum()
+    return float(x.size * x.max() / tot) if tot > 0 else float("nan")
+
+
+def entropy_deficit(x) -> float:
+    """Normalized entropy deficit 1 - H(pi) / log n of the load distribution
+    pi = x / sum x, with 0 log 0 = 0 (p5 Section 10.2); NaN for an all-zero vector."""
+    x = _f64(x)
+    tot = x.sum()
+    if tot <= 0:
+        return float("nan")
+    pi = x / tot
+    nz = pi[pi > 0]
+    H = float(-(nz * np.log(nz)).sum())
+    return 1.0 - H / math.log(x.size)
+
+
+def coefficient_of_variation(x) -> float:
+    """Standard deviation over mean of the counts (population form; p5 Section 10.2)."""
+    x = _f64(x)
+    m = x.mean()
+    return float(x.std() / m) if m > 0 else float("nan")
+
+
+@dataclass
+class BalanceStats:
+    f: np.ndarray                 # [N] requested-route fractions C_req / (K T)
+    P: np.ndarray                 # [N] mean normalized router scores
+    lbl: float                    # N f . P (p5 Eq. 30)
+    imax_req: float               # Eq. 39 on requested counts
+    imax_keep: float              # Eq. 22 on kept counts
+    ih_req: float                 # entropy deficit of requested counts
+    ih_keep: float                # entropy deficit of kept counts
+    cv_req: float
+    cv_keep: float
+    never_selected: int           # experts with no requested route
+    delta_route: float            # dropped / requested routes (p5 Eq. 27)
+    tokens_lost_any: int          # tokens with at least one dropped route
+    tokens_lost_all: int          # tokens whose K routes were all dropped
+    weight_removed: float         # dropped share of the selected coefficient mass
+
+
+def balance_stats(p, idx, kept, r, N: int) -> BalanceStats:
+    """Forward balance and drop statistics of one routed batch: the hard and soft
+    marginals f and P and the Switch-style scalar N f.P (p5 Eq. 38, 30); requested and
+    kept max/mean imbalance, entropy deficit, coefficient of variation and never-selected
+    count (p5 Eq. 22, 39, Section 10.2); the route-drop fraction (Eq. 27) and, as Section
+    10.3 asks, the tokens losing at least one and all K routes and the selected mixture
+    weight removed. `p` are the normalized scores, `kept` the kept-route mask and `r` the
+    routed coefficients of the selected slots."""
+    p = _f64(p)
+    idx = np.asarray(idx)
+    kept = np.asarray(kept, dtype=bool)
+    r = _f64(r)
+    T, K = idx.shape
+    C_req = requested_counts(idx, N)
+    C_keep = np.bincount(idx[kept].reshape(-1), minlength=N).astype(np.int64)
+    f = C_req / float(K * T)
+    P = p.mean(axis=0)
+    lbl = float(N * f @ P)
+    dropped = ~kept
+    n_drop = dropped.sum(axis=1)
+    sel = r.sum()
+    return BalanceStats(
+        f=f, P=P, lbl=lbl,
+        imax_req=imbalance_max(C_req), imax_keep=imbalance_max(C_keep),
+        ih_req=entropy_deficit(C_req), ih_keep=entropy_deficit(C_keep),
+        cv_req=coefficient_of_variation(C_req), cv_keep=coefficient_of_variation(C_keep),
+        never_selected=int((C_req == 0).sum()),
+        delta_route=float(dropped.sum() / float(K * T)),
+        tokens_lost_any=int((n_drop > 0).sum()),
+        tokens_lost_all=int((n_drop == K).sum()),
+        weight_removed=float(r[dropped].sum() / sel) if sel > 0 else float("nan"),
+    )
+
+
+# ----------------------------------------------------------------------------------------
 # a5-a7: SwiGLU experts
 # ----------------------------------------------------------------------------------------
 def swiglu(X, w_gate, w_up, w_down):

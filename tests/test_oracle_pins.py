@@ -479,3 +479,106 @@ def test_planted_mistake_is_caught(name, monkeypatch):
                 pin(-1)
             else:
                 pin()
+
+
+# ---------------------------------------------------------------------------------------
+# f1: balance statistics and drop diagnostics
+# ---------------------------------------------------------------------------------------
+def _frac(v):
+    from fractions import Fraction
+    return float(Fraction(v))
+
+
+def test_six_token_counterexample_eq43_45():
+    """p5 Eq. 43-45: two experts, top-1, six tokens: C_req = (2, 4), f = (1/3, 2/3),
+    P = (3/5, 2/5), I_max^req = 4/3 and LBL = 14/15 < 1."""
+    g = json.load(open(os.path.join(GOLD, "eq43_six_token_lbl.json")))
+    p = np.array(g["normalized_scores"])
+    idx = O.topk_select(p, g["K"])                     # the winner of each token
+    kept = np.ones_like(idx, dtype=bool)              # no capacity filter
+    r = np.take_along_axis(p, idx, axis=1)
+    st = O.balance_stats(p, idx, kept, r, g["N"])
+    assert np.array_equal(O.requested_counts(idx, g["N"]), g["C_req"])
+    assert np.allclose(st.f, [_frac(v) for v in g["f"]], rtol=0, atol=1e-15)
+    assert np.allclose(st.P, [_frac(v) for v in g["P"]], rtol=0, atol=1e-15)
+    assert abs(st.imax_req - _frac(g["imax_req"])) < 1e-15
+    assert abs(st.lbl - _frac(g["lbl"])) < 1e-15
+    assert st.never_selected == 0 and st.delta_route == 0.0 and st.tokens_lost_any == 0
+
+
+def test_uniform_scores_give_lbl_one_for_any_selection_eq42():
+    """p5 Eq. 42: P uniform => LBL = 1 for every requested-route fraction f, including a
+    collapsed one (every token picks expert 0 on all-tied logits)."""
+    rng = np.random.default_rng(5)
+    T, N, K = 50, 8, 2
+    z = np.zeros((T, N))
+    for idx in (O.topk_select(z, K), np.stack([rng.choice(N, K, replace=False) for _ in range(T)])):
+        p = O.normalized_scores(z, O.SOFTMAX)
+        st = O.balance_stats(p, idx, np.ones((T, K), bool), np.full((T, K), 0.5), N)
+        assert abs(st.lbl - 1.0) < 1e-12
+
+
+def test_lbl_centered_form_eq41():
+    """p5 Eq. 41: LBL = 1 + N (f - u).(P - u) = 1 + N^2 Cov_i(f_i, P_i)."""
+    rng = np.random.default_rng(9)
+    for score in (O.SOFTMAX, O.SIGMOID):
+        T, N, K = 300, 16, 4
+        z = rng.standard_normal((T, N)) * 2
+        idx = O.topk_select(z + rng.standard_normal(N), K)
+        p = O.normalized_scores(z, score)
+        st = O.balance_stats(p, idx, np.ones((T, K), bool), np.ones((T, K)), N)
+        u = np.full(N, 1.0 / N)
+        assert abs(st.lbl - (1 + N * (st.f - u) @ (st.P - u))) < 1e-12
+        cov = np.mean((st.f - st.f.mean()) * (st.P - st.P.mean()))
+        assert abs(st.lbl - (1 + N * N * cov)) < 1e-12
+        assert abs(st.f.sum() - 1) < 1e-12 and abs(st.P.sum() - 1) < 1e-12   # Eq. 38
+
+
+def test_normalized_scores_rows_are_distributions():
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((7, 5))
+    for score in (O.SOFTMAX, O.SIGMOID, O.SOFTMAX_SELECTED):
+        p = O.normalized_scores(z, score)
+        assert np.allclose(p.sum(1), 1.0) and np.all(p > 0)
+    sig = 1 / (1 + np.exp(-z))
+    assert np.allclose(O.normalized_scores(z, O.SIGMOID), sig / sig.sum(1, keepdims=True))
+
+
+def test_imbalance_entropy_cv_closed_forms():
+    """p5 Eq. 22 and Section 10.2: uniform load -> I_max = 1, entropy deficit 0, CV 0;
+    one-hot load over n -> I_max = n, deficit 1; two-valued example by hand."""
+    assert O.imbalance_max([3, 3, 3, 3]) == 1.0
+    assert abs(O.entropy_deficit([3, 3, 3, 3])) < 1e-15
+    assert O.coefficient_of_variation([3, 3, 3, 3]) == 0.0
+    assert O.imbalance_max([0, 0, 7, 0]) == 4.0
+    assert abs(O.entropy_deficit([0, 0, 7, 0]) - 1.0) < 1e-15
+    # x = (1, 3): pi = (1/4, 3/4), H = -(1/4 ln 1/4 + 3/4 ln 3/4), deficit = 1 - H / ln 2
+    H = -(0.25 * math.log(0.25) + 0.75 * math.log(0.75))
+    assert abs(O.entropy_deficit([1, 3]) - (1 - H / math.log(2))) < 1e-15
+    assert O.imbalance_max([1, 3]) == 1.5
+    assert abs(O.coefficient_of_variation([1, 3]) - 0.5) < 1e-15      # std 1, mean 2
+
+
+def test_drop_diagnostics_capacity_edges():
+    """p5 Eq. 27 and Section 10.3: unlimited capacity drops nothing; capacity 0 drops every
+    route, so every token loses all K and the whole selected weight; capacity 1 on a
+    collapsed router keeps exactly one route of one token."""
+    rng = np.random.default_rng(3)
+    T, N, K = 40, 6, 3
+    z = rng.standard_normal((T, N))
+    idx = O.topk_select(z, K)
+    r = O.route_coefficients(z, idx, O.SOFTMAX, True, 1.0)
+    p = O.normalized_scores(z, O.SOFTMAX)
+    st = O.balance_stats(p, idx, O.keep_routes(idx, N, -1), r, N)
+    assert st.delta_route == 0 and st.tokens_lost_any == 0 and st.weight_removed == 0
+    st = O.balance_stats(p, idx, O.keep_routes(idx, N, 0), r, N)
+    assert st.delta_route == 1 and st.tokens_lost_all == T and st.tokens_lost_any == T
+    assert abs(st.weight_removed - 1) < 1e-15 and math.isnan(st.imax_keep)
+    z0 = np.zeros((T, N))
+    idx0 = O.topk_select(z0, K)                        # all tokens pick experts 0..K-1
+    st = O.balance_stats(O.normalized_scores(z0, O.SOFTMAX), idx0, O.keep_routes(idx0, N, 1),
+                         np.full((T, K), 1.0 / K), N)
+    assert st.never_selected == N - K
+    # token 0 keeps its K routes (one per expert); every later token loses all K
+    assert st.tokens_lost_any == T - 1 and st.tokens_lost_all == T - 1
+    assert abs(st.delta_route - (K * T - K) / (K * T)) < 1e-15
