@@ -220,6 +220,8 @@ def entropy_deficit(x) -> float:
     tot = x.sum()
     if tot <= 0:
         return float("nan")
+    if x.size == 1:
+        return 0.0      # a single expert carries the whole load: balanced, log n = 0
     pi = x / tot
     nz = pi[pi > 0]
     H = float(-(nz * np.log(nz)).sum())

@@ -557,6 +557,9 @@ def test_imbalance_entropy_cv_closed_forms():
     assert abs(O.entropy_deficit([1, 3]) - (1 - H / math.log(2))) < 1e-15
     assert O.imbalance_max([1, 3]) == 1.5
     assert abs(O.coefficient_of_variation([1, 3]) - 0.5) < 1e-15      # std 1, mean 2
+    # one expert: the whole load on it is balanced (I_max 1, CV 0, deficit taken as 0)
+    assert O.imbalance_max([5]) == 1.0 and O.coefficient_of_variation([5]) == 0.0
+    assert O.entropy_deficit([5]) == 0.0 and math.isnan(O.entropy_deficit([0]))
 
 
 def test_drop_diagnostics_capacity_edges():
