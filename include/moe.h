@@ -246,6 +246,52 @@ int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
                 const float* s_tok, void* y, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_balance_stats: forward balance statistics and drop diagnostics of one routed
+ * batch ("Section 10: Routing, Capacity, and Load Balancing"):
+ *   P[i]   = (1/T) sum_t p_{t,i}, the mean of each token's scores normalized across all
+ *            N experts (Eq. 38): full softmax of the logits for the softmax modes, sigmoid
+ *            affinities divided by their sum for MOE_SCORE_SIGMOID
+ *   stats[MOE_STAT_LBL]         N sum_i f_i P_i with f_i = C_req[i] / (K T)   (Eq. 30)
+ *   stats[MOE_STAT_IMAX_REQ|KEEP]  N max_i C[i] / sum_i C[i]  (Eq. 39, Eq. 22)
+ *   stats[MOE_STAT_IH_REQ|KEEP]    1 - H(C / sum C) / ln N, entropy deficit (Section 10.2);
+ *                                  0 when N = 1 (one expert is balanced by construction)
+ *   stats[MOE_STAT_CV_REQ|KEEP]    std / mean of the counts (population)
+ *   stats[MOE_STAT_NEVER_SELECTED] experts with C_req = 0
+ *   stats[MOE_STAT_DELTA_ROUTE]    (K T - sum C_keep) / (K T)                  (Eq. 27)
+ *   stats[MOE_STAT_TOKENS_LOST_ANY|ALL] tokens with >= 1 / all K routes dropped (Sec. 10.3)
+ *   stats[MOE_STAT_WEIGHT_REMOVED] dropped share of the selected coefficient mass sum r
+ * Ratios of an all-zero count vector are NaN. Sums run in a fixed order (repeatable).
+ *
+ *   logits             [T][N] float32 router logits as moe_route writes them (bias added)
+ *   C_req, C_keep      [N] int32 (moe_permute); dest_row, topk_r [T][K]
+ *   P                  [N] float32 out; stats [MOE_STAT_COUNT] float32 out
+ *   workspace          moe_balance_stats_workspace_size(T, N) bytes
+ * All buffers are device memory owned by the caller. Returns MOE_ERR_INVALID_ARG for
+ * K > N, a non-positive size, an unknown score mode or a NULL buffer, MOE_ERR_UNSUPPORTED
+ * for N > 256 or K > 16, MOE_ERR_WORKSPACE for a short workspace; T = 0 enqueues nothing.
+ * ------------------------------------------------------------------------------- */
+enum moe_stat {
+  MOE_STAT_LBL = 0,
+  MOE_STAT_IMAX_REQ = 1,
+  MOE_STAT_IMAX_KEEP = 2,
+  MOE_STAT_IH_REQ = 3,
+  MOE_STAT_IH_KEEP = 4,
+  MOE_STAT_CV_REQ = 5,
+  MOE_STAT_CV_KEEP = 6,
+  MOE_STAT_NEVER_SELECTED = 7,
+  MOE_STAT_DELTA_ROUTE = 8,
+  MOE_STAT_TOKENS_LOST_ANY = 9,
+  MOE_STAT_TOKENS_LOST_ALL = 10,
+  MOE_STAT_WEIGHT_REMOVED = 11,
+  MOE_STAT_COUNT = 12
+};
+size_t moe_balance_stats_workspace_size(int T, int N);
+int moe_balance_stats(int T, int N, int K, int score, const float* logits, const int32_t* C_req,
+                      const int32_t* C_keep, const int32_t* dest_row, const float* topk_r,
+                      float* P, float* stats, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_forward: the whole layer: route -> permute -> grouped SwiGLU experts -> shared
  * MLP -> combine, all enqueued on `stream` with no host synchronization (counts and
  * offsets stay on the device).
@@ -289,6 +335,10 @@ typedef struct moe_forward_args {
   void* h_perm;          /* [rows][d_r] */
   void* f_perm;          /* [rows][d_model] */
   void* g;               /* [T][d_model] shared output */
+  /* Balance statistics (moe_balance_stats) of the same batch, computed after the combine
+   * when both are non-NULL (one without the other is MOE_ERR_INVALID_ARG): */
+  float* balance_P;      /* [N] */
+  float* balance_stats;  /* [MOE_STAT_COUNT] */
 } moe_forward_args;
 
 size_t moe_forward_workspace_size(const moe_forward_args* args);

@@ -74,6 +74,8 @@ struct FwdWs {
   float* s_tok;
   int32_t *hist, *loc_rank, *C_req, *C_keep, *offsets, *dest_row, *row_token;
   void *x_perm, *h_perm, *f_perm, *g, *h_shared;
+  float* logits;     // needed by the balance statistics
+  void* stats_ws;
 };
 
 size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
@@ -103,6 +105,9 @@ size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
     w.g = nullptr;
     w.h_shared = nullptr;
   }
+  const bool stats = a->balance_P != nullptr && a->balance_stats != nullptr;
+  w.logits = a->logits ? a->logits : (stats ? c.take<float>(T * N) : nullptr);
+  w.stats_ws = stats ? static_cast<void*>(c.take<char>(stats_workspace_bytes(a->T, a->N))) : nullptr;
   if (out) *out = w;
   return c.off;
 }
@@ -369,6 +374,28 @@ int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
   return MOE_OK;
 }
 
+size_t moe_balance_stats_workspace_size(int T, int N) {
+  if (T <= 0 || N <= 0) return 0;
+  return stats_workspace_bytes(T, N);
+}
+
+int moe_balance_stats(int T, int N, int K, int score, const float* logits, const int32_t* C_req,
+                      const int32_t* C_keep, const int32_t* dest_row, const float* topk_r,
+                      float* P, float* stats, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (T < 0 || N <= 0 || K <= 0 || K > N) return MOE_ERR_INVALID_ARG;
+  if (N > moe::kMaxN || K > moe::kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (!logits || !C_req || !C_keep || !dest_row || !topk_r || !P || !stats)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < moe_balance_stats_workspace_size(T, N))
+    return MOE_ERR_WORKSPACE;
+  MOE_HIP(launch_balance_stats(T, N, K, score, logits, dest_row, topk_r, C_req, C_keep, P, stats,
+                               workspace, stream));
+  return MOE_OK;
+}
+
 size_t moe_forward_workspace_size(const moe_forward_args* a) {
   if (!a || a->T <= 0 || a->N <= 0 || a->K <= 0 || a->d_model <= 0) return 0;
   return carve_forward(a, nullptr, nullptr);
@@ -388,6 +415,7 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   if (a->w_shared_gate && a->d_s == 0) return MOE_ERR_INVALID_ARG;
   if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_ERR_INVALID_ARG;
   if (a->weights_packed && a->dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((a->balance_P == nullptr) != (a->balance_stats == nullptr)) return MOE_ERR_INVALID_ARG;
   if (a->T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_forward_workspace_size(a)) return MOE_ERR_WORKSPACE;
   FwdWs w{};
@@ -395,7 +423,7 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   const int T = a->T, d = a->d_model, N = a->N, K = a->K;
   const int rows = moe_max_rows(T, N, K, a->capacity);
   MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
-                       a->logit_bias, a->w_shared_gate, a->logits, 0, w.topk_idx, w.topk_r,
+                       a->logit_bias, a->w_shared_gate, w.logits, 0, w.topk_idx, w.topk_r,
                        w.s_tok, stream));
   MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, a->capacity, w.hist, w.C_req, w.C_keep, w.offsets, stream));
@@ -406,6 +434,9 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
                         a->ws_up, a->ws_down, w.h_perm, w.f_perm, w.h_shared, w.g, 0, stream));
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));
+  if (w.stats_ws != nullptr)
+    MOE_HIP(launch_balance_stats(T, N, K, a->score, w.logits, w.dest_row, w.topk_r, w.C_req,
+                                 w.C_keep, a->balance_P, a->balance_stats, w.stats_ws, stream));
   return MOE_OK;
 }
 

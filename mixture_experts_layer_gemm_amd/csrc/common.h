@@ -73,6 +73,12 @@ hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* 
                           const int32_t* offsets, int32_t* dest_row, int32_t* row_token,
                           void* x_perm, hipStream_t stream);
 
+size_t stats_workspace_bytes(int T, int N);
+hipError_t launch_balance_stats(int T, int N, int K, int score, const float* logits,
+                                const int32_t* dest_row, const float* topk_r,
+                                const int32_t* C_req, const int32_t* C_keep, float* P,
+                                float* stats, void* workspace, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(bool swiglu, int G, int K_dim, int N_dim, int dt, const void* a,
                                const int32_t* row_index, const int32_t* offsets, int max_rows,
                                const void* w0, const void* w1, void* out, hipStream_t stream);

@@ -37,7 +37,13 @@ class ForwardArgs(ctypes.Structure):
         (n, c_void_p) for n in ("x", "w_router", "logit_bias", "w_shared_gate", "w_gate", "w_up",
                                 "w_down", "ws_gate", "ws_up", "ws_down", "y", "logits", "topk_idx",
                                 "topk_r", "s_tok", "C_req", "C_keep", "offsets", "dest_row",
-                                "row_token", "x_perm", "h_perm", "f_perm", "g")]
+                                "row_token", "x_perm", "h_perm", "f_perm", "g", "balance_P",
+                                "balance_stats")]
+
+# order of moe_balance_stats' output vector (enum moe_stat)
+STAT_NAMES = ["lbl", "imax_req", "imax_keep", "ih_req", "ih_keep", "cv_req", "cv_keep",
+              "never_selected", "delta_route", "tokens_lost_any", "tokens_lost_all",
+              "weight_removed"]
 
 
 def _load() -> ctypes.CDLL:
@@ -59,6 +65,8 @@ def _load() -> ctypes.CDLL:
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
         "moe_experts": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, I, P]),
+        "moe_balance_stats_workspace_size": (S, [I, I]),
+        "moe_balance_stats": (I, [I, I, I, I, P, P, P, P, P, P, P, P, S, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
         "moe_forward": (I, [POINTER(ForwardArgs), P, S, P]),
     }
@@ -246,6 +254,28 @@ def moe_experts(x, row_token, offsets, max_rows: int, w_gate, w_up, w_down, shar
     return out
 
 
+def moe_balance_stats(logits, C_req, C_keep, dest_row, topk_r, score: int = SCORE_SOFTMAX):
+    """Balance statistics and drop diagnostics of one routed batch: returns (P, stats)
+    with P the [N] mean normalized scores and stats a dict keyed by STAT_NAMES (device
+    tensors; read them after the stream synchronizes)."""
+    T, N = logits.shape
+    K = dest_row.shape[1]
+    dev = logits.device
+    P = torch.empty(N, dtype=torch.float32, device=dev)
+    st = torch.empty(len(STAT_NAMES), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.moe_balance_stats_workspace_size(T, N), dev)
+    rc = lib.moe_balance_stats(T, N, K, score, _ptr(logits), _ptr(C_req), _ptr(C_keep),
+                               _ptr(dest_row), _ptr(topk_r), _ptr(P), _ptr(st), _ptr(ws),
+                               ws.numel(), _stream())
+    _check("moe_balance_stats", rc)
+    return P, st
+
+
+def stats_dict(st: torch.Tensor) -> dict:
+    v = st.cpu().tolist()
+    return dict(zip(STAT_NAMES, v))
+
+
 def moe_combine(f_perm, dest_row, topk_r, g=None, s: float = 1.0, s_tok=None, y=None):
     T, K = dest_row.shape
     d = f_perm.shape[1]
@@ -275,7 +305,7 @@ class MoELayer:
     def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
                  logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
-                 pack_weights=None, keep_x_perm=False):
+                 pack_weights=None, keep_x_perm=False, balance_stats=False):
         self.x = x
         T, d = x.shape
         N, d_r, _ = w_gate.shape
@@ -322,6 +352,11 @@ class MoELayer:
                 t = torch.empty(*shape, dtype=dtype, device=dev)
                 self.out[name] = t
                 setattr(a, name, t.data_ptr())
+        if balance_stats:       # f and drop diagnostics of every forward (moe_balance_stats)
+            self.out["balance_P"] = torch.empty(N, dtype=torch.float32, device=dev)
+            self.out["balance_stats"] = torch.empty(len(STAT_NAMES), dtype=torch.float32, device=dev)
+            a.balance_P = self.out["balance_P"].data_ptr()
+            a.balance_stats = self.out["balance_stats"].data_ptr()
         self.args = a
         self.ws = _workspace(lib.moe_forward_workspace_size(ctypes.byref(a)), dev)
 

@@ -9,7 +9,8 @@ from mixture_experts_layer_gemm_amd import moe
 from mixture_experts_layer_gemm_amd import synth
 import oracle.moe_oracle as O
 
-EXPECTED = ["moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
+EXPECTED = ["moe_balance_stats", "moe_balance_stats_workspace_size",
+            "moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
             "moe_forward_workspace_size",
             "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_pack_weights", "moe_permute",
             "moe_permute_workspace_size",
@@ -102,6 +103,13 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 1, 1, 0, 1, None, 8, 1, 1, 1, None) == \
         moe.MOE_ERR_INVALID_ARG                               # row index needs a_rows
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
+    bs = [64, 8, 2, 0, 1, 1, 1, 1, 1, 1, 1]
+    assert L.moe_balance_stats(*bs, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_balance_stats(64, 8, 9, *bs[3:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG  # K > N
+    assert L.moe_balance_stats(64, 300, 2, *bs[3:], 1, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_balance_stats(*bs[:4], None, *bs[5:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_stats(0, *bs[1:], None, 0, None) == moe.MOE_OK
+    assert moe.lib.moe_balance_stats_workspace_size(4096, 64) >= 64 * 64 * 4
     ex = [8, 512, 512, 512, 1, 1, 1, 64, 1, 1, 64, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1]
     assert L.moe_experts(*ex, 3, None) == moe.MOE_ERR_INVALID_ARG          # pass out of range
     assert L.moe_experts(*ex[:5], 2, *ex[6:], 0, None) == moe.MOE_ERR_INVALID_ARG  # packed 0/1
@@ -126,6 +134,8 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
     args.K, args.T = 2, 0
     assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_OK
+    args.balance_P = 1                                        # P without the stats vector
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_synth_streams_are_deterministic_and_bf16_exact():
