@@ -133,7 +133,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
-              "unsharded on a single MI355X (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "unsharded on a single MI355X; expert-parallel sharding across GPUs is not built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

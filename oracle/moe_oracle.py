@@ -19,7 +19,7 @@ in row-vector form, E(x) = [SiLU(x W_g) * (x W_u)] W_d (p4, Eq. 74); here
 ``w_gate = W_g^T`` with shape [d_ff, d_model], ``w_up = W_u^T`` [d_ff, d_model] and
 ``w_down = W_d^T`` [d_model, d_ff].
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   * top-K ties go to the lower expert index; -0.0 and +0.0 compare equal;
   * the K output slots of a token are ordered by descending key, ties by index;
   * selection uses the (biased) logit for every score function;
@@ -157,6 +157,82 @@ def keep_routes(idx, N: int, capacity: int) -> np.ndarray:
     return kept
 
 
+# ----------------------------------------------------------------------------------------
+# f2: rank-wide capacity (one budget shared by the experts of a destination group)
+# ----------------------------------------------------------------------------------------
+def rank_capacity_from_factor(c: float, K: int, T_s: int) -> int:
+    """Destination-rank budget C_rank = max(1, ceil(c T_route)) with T_route = K T_s, the
+    routes one source rank produces (p5 Eq. 23)."""
+    return max(1, int(math.ceil(float(c) * K * T_s)))
+
+
+def destination_of(N: int, group: int) -> np.ndarray:
+    """rho(i): the destination that owns expert i when consecutive groups of `group`
+    experts share a destination (p5 Eq. 20)."""
+    if group <= 0 or N % group:
+        raise ValueError("every destination owns the same number of experts")
+    return np.arange(N) // group
+
+
+def rank_loads(C, group: int) -> np.ndarray:
+    """R_q = sum of the counts of the experts destination q owns (p5 Eq. 20 for requested
+    counts, Eq. 21 for kept counts)."""
+    C = np.asarray(C)
+    rho = destination_of(len(C), group)
+    return np.bincount(rho, weights=C, minlength=int(rho.max()) + 1).astype(np.int64)
+
+
+def split_requested_counts(idx, N: int, n_sources: int) -> np.ndarray:
+    """C_{s,i}^req (p5 Eq. 19) when the batch's tokens are split, in index order, into
+    n_sources contiguous source shards (np.array_split sizes)."""
+    idx = np.asarray(idx)
+    shards = np.array_split(np.arange(idx.shape[0]), n_sources)
+    return np.stack([requested_counts(idx[sh], N) for sh in shards])
+
+
+def keep_routes_rank_wide(idx, N: int, group: int, budget: int, n_sources: int = 1) -> np.ndarray:
+    """Kept-route mask under rank-wide capacity (p5 Section 10.3, Eq. 23): each
+    destination q owns `group` consecutive experts and one shared budget. Its requested
+    split counts are flattened local-expert-major, then source-rank order; routes are
+    admitted cumulatively until the budget is reached, and inside each (source, expert)
+    split the admitted routes are a prefix in token order. A negative budget keeps
+    every route. Sources are the n_sources contiguous token shards."""
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    if budget < 0:
+        return np.ones((T, K), dtype=bool)
+    rho = destination_of(N, group)
+    shards = np.array_split(np.arange(T), n_sources)
+    C = split_requested_counts(idx, N, n_sources)           # [S, N]
+    admit = np.zeros_like(C)                               # C_{s,i}^keep
+    for q in range(int(rho.max()) + 1):
+        room = budget
+        for e in np.flatnonzero(rho == q):                 # local-expert-major
+            for s in range(n_sources):                     # then source-rank order
+                admit[s, e] = min(C[s, e], room)
+                room -= admit[s, e]
+    kept = np.zeros((T, K), dtype=bool)
+    for s, sh in enumerate(shards):
+        taken = np.zeros(N, dtype=np.int64)
+        for t in sh:                                       # prefix of each split
+            for k in range(K):
+                e = int(idx[t, k])
+                if taken[e] < admit[s, e]:
+                    kept[t, k] = True
+                    taken[e] += 1
+    return kept
+
+
+def drops_rank_wide(C_req, budget: int) -> int:
+    """D^rank = [sum_j C_j^req - B]_+ for the local experts of one destination (p5 Eq. 28)."""
+    return max(int(np.sum(C_req)) - int(budget), 0)
+
+
+def drops_per_expert(C_req, budgets) -> int:
+    """D^expert = sum_j [C_j^req - b_j]_+ under independent expert budgets (p5 Eq. 28)."""
+    return int(sum(max(int(c) - int(b), 0) for c, b in zip(C_req, budgets)))
+
+
 @dataclass
 class Permutation:
     C_keep: np.ndarray        # [N]   M_i, rows presented to expert i (p5 Eq. 21)
@@ -251,16 +327,20 @@ class BalanceStats:
     tokens_lost_any: int          # tokens with at least one dropped route
     tokens_lost_all: int          # tokens whose K routes were all dropped
     weight_removed: float         # dropped share of the selected coefficient mass
+    imax_rank_req: float = float("nan")    # Eq. 22 on requested destination totals (Eq. 20)
+    imax_rank_keep: float = float("nan")   # Eq. 22 on kept destination totals (Eq. 21)
 
 
-def balance_stats(p, idx, kept, r, N: int) -> BalanceStats:
+def balance_stats(p, idx, kept, r, N: int, group: int = 0) -> BalanceStats:
     """Forward balance and drop statistics of one routed batch: the hard and soft
     marginals f and P and the Switch-style scalar N f.P (p5 Eq. 38, 30); requested and
     kept max/mean imbalance, entropy deficit, coefficient of variation and never-selected
     count (p5 Eq. 22, 39, Section 10.2); the route-drop fraction (Eq. 27) and, as Section
     10.3 asks, the tokens losing at least one and all K routes and the selected mixture
     weight removed. `p` are the normalized scores, `kept` the kept-route mask and `r` the
-    routed coefficients of the selected slots."""
+    routed coefficients of the selected slots. With `group` > 0, consecutive groups of
+    that many experts form the destinations, and the max/mean imbalance of their
+    requested and kept totals is the rank-level pair of p5 Eq. 22 (Table 17)."""
     p = _f64(p)
     idx = np.asarray(idx)
     kept = np.asarray(kept, dtype=bool)
@@ -284,6 +364,8 @@ def balance_stats(p, idx, kept, r, N: int) -> BalanceStats:
         tokens_lost_any=int((n_drop > 0).sum()),
         tokens_lost_all=int((n_drop == K).sum()),
         weight_removed=float(r[dropped].sum() / sel) if sel > 0 else float("nan"),
+        imax_rank_req=imbalance_max(rank_loads(C_req, group)) if group > 0 else float("nan"),
+        imax_rank_keep=imbalance_max(rank_loads(C_keep, group)) if group > 0 else float("nan"),
     )
 
 

@@ -585,3 +585,139 @@ def test_drop_diagnostics_capacity_edges():
     # token 0 keeps its K routes (one per expert); every later token loses all K
     assert st.tokens_lost_any == T - 1 and st.tokens_lost_all == T - 1
     assert abs(st.delta_route - (K * T - K) / (K * T)) < 1e-15
+
+
+# ---------------------------------------------------------------------------------------
+# f2: rank-wide capacity
+# ---------------------------------------------------------------------------------------
+with open(os.path.join(GOLD, "fig41_rank_wide_capacity.json")) as _f:
+    FIG41 = json.load(_f)
+
+
+def _tokens_for_requests(req):
+    """K = 1 routing in which expert j is chosen by req[j] consecutive tokens."""
+    return np.repeat(np.arange(len(req)), req).reshape(-1, 1)
+
+
+def test_fig41_rank_wide_vs_per_expert():
+    """p5 Figure 41 / Table 18 report example: with six rows per destination rank, one
+    shared budget keeps all 12 routes; three private rows per expert keep 10, drop two
+    E0 routes and leave two E1 rows unused."""
+    g = FIG41
+    req = np.array(g["requests"])
+    N, grp, B, b = len(req), g["experts_per_rank"], g["rank_budget"], g["expert_budget"]
+    idx = _tokens_for_requests(req)
+    kr = O.keep_routes_rank_wide(idx, N, grp, B)
+    ke = O.keep_routes(idx, N, b)
+    assert int(kr.sum()) == g["rank_wide"]["kept"] and int((~kr).sum()) == g["rank_wide"]["dropped"]
+    assert int(ke.sum()) == g["per_expert"]["kept"] and int((~ke).sum()) == g["per_expert"]["dropped"]
+    keep_e = np.bincount(idx[ke], minlength=N)
+    assert int(np.maximum(b - keep_e, 0).sum()) == g["per_expert"]["unused_rows"]
+    keep_r = O.rank_loads(np.bincount(idx[kr], minlength=N), grp)
+    assert int(np.maximum(B - keep_r, 0).sum()) == g["rank_wide"]["unused_rows"]
+    # the routes only pooling admits: E0's fourth and fifth requests
+    only = kr[:, 0] & ~ke[:, 0]
+    assert int(only.sum()) == g["pooling_only_routes_of_E0"] and set(np.flatnonzero(only)) == {3, 4}
+    C = O.requested_counts(idx, N)
+    d_rank = [O.drops_rank_wide(C[q * grp:(q + 1) * grp], B) for q in range(N // grp)]
+    d_exp = [O.drops_per_expert(C[q * grp:(q + 1) * grp], [b] * grp) for q in range(N // grp)]
+    assert d_rank == g["eq28_drops"]["rank_wide"] and d_exp == g["eq28_drops"]["per_expert"]
+
+
+def test_rank_wide_drops_follow_eq28_and_eq29():
+    """p5 Eq. 28-29: the admission procedure drops exactly [sum_j C_j - B]_+ per
+    destination, never more than matched independent budgets (sum_j b_j = B), and
+    strictly fewer when a hot expert overflows while a neighbour leaves rows unused."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        grp = int(rng.integers(1, 5))
+        N = grp * int(rng.integers(1, 4))
+        T, K = int(rng.integers(1, 40)), int(rng.integers(1, N + 1))
+        z = rng.standard_normal((T, N)) + rng.exponential(2.0, N)   # skewed experts
+        idx = O.topk_select(z, K)
+        b = rng.integers(0, 2 * T // max(1, N // K) + 2, size=N)
+        for q in range(N // grp):
+            lo, hi = q * grp, (q + 1) * grp
+            B = int(b[lo:hi].sum())
+            kept = O.keep_routes_rank_wide(idx, N, grp, B, n_sources=int(rng.integers(1, 4)))
+            C = O.requested_counts(idx, N)[lo:hi]
+            mine = (idx >= lo) & (idx < hi)
+            D_rank = int((mine & ~kept).sum())
+            assert D_rank == O.drops_rank_wide(C, B)
+            D_exp = O.drops_per_expert(C, b[lo:hi])
+            assert D_rank <= D_exp
+            if np.any(C > b[lo:hi]) and np.any(C < b[lo:hi]):
+                assert D_rank < D_exp
+
+
+def test_rank_wide_admission_is_expert_major_prefix():
+    """p5 Section 10.3: with contiguous source shards in rank order, local-expert-major
+    then source-rank flattening with a prefix per split is the same as admitting the
+    routes of each destination in (expert, token) order; so the kept mask does not
+    depend on how many sources the batch is split into. With one expert per
+    destination it is the independent per-expert capacity with the same budget."""
+    rng = np.random.default_rng(5)
+    T, N, K = 90, 12, 3
+    z = rng.standard_normal((T, N)) + np.linspace(2, 0, N)
+    idx = O.topk_select(z, K)
+    for grp in (1, 2, 3, 4, 6, 12):
+        B = 40 if grp > 1 else 15
+        masks = [O.keep_routes_rank_wide(idx, N, grp, B, n_sources=s) for s in (1, 2, 3, 7)]
+        for m in masks[1:]:
+            assert np.array_equal(m, masks[0])
+        # the same mask by hand: the first B routes of each destination in (expert, token)
+        exp = np.zeros_like(masks[0])
+        for q in range(N // grp):
+            order = sorted(((int(idx[t, k]), t, k) for t in range(T) for k in range(K)
+                            if q * grp <= idx[t, k] < (q + 1) * grp))
+            for e, t, k in order[:B]:
+                exp[t, k] = True
+        assert np.array_equal(masks[0], exp)
+    assert np.array_equal(O.keep_routes_rank_wide(idx, N, 1, 15), O.keep_routes(idx, N, 15))
+    assert O.keep_routes_rank_wide(idx, N, 4, -1).all()
+
+
+def test_rank_capacity_eq23_and_hot_expert_fit_eq24():
+    """p5 Eq. 23: C_rank = max(1, ceil(c K T_s)); Eq. 24: a hot expert whose neighbours
+    are cold can take the whole budget, c N_local times the balanced per-expert mean."""
+    assert O.rank_capacity_from_factor(1.0, 4, 1000) == 4000
+    assert O.rank_capacity_from_factor(1.25, 4, 1001) == 5005
+    assert O.rank_capacity_from_factor(0.0, 4, 1000) == 1
+    assert O.rank_capacity_from_factor(1e-6, 1, 10) == 1
+    T, N, grp, c = 256, 16, 4, 1.0
+    M_E = N // grp                                # destinations, and as many equal sources
+    T_s = T // M_E
+    B = O.rank_capacity_from_factor(c, 1, T_s)    # K = 1: T_route = T_s
+    assert B == 64
+    idx = np.zeros((T, 1), dtype=np.int64)        # every token on expert 0
+    kept = O.keep_routes_rank_wide(idx, N, grp, B, n_sources=M_E)
+    balanced_mean = T_s / grp                     # T_route / N_local
+    assert int(kept.sum()) == B and B / balanced_mean == c * grp
+    # per-expert budgets of Eq. 25 hold the same expert to ceil(c T_route / N_local)
+    assert int(O.keep_routes(idx, N, int(math.ceil(c * T_s / grp))).sum()) == 16
+
+
+def test_rank_level_imbalance():
+    """p5 Eq. 20-22, Table 17: destination totals sum the experts each destination owns;
+    one destination is trivially balanced and one expert per destination gives back the
+    expert-level ratio; a balanced total can hide a concentrated destination."""
+    C = np.array([6, 0, 3, 3])
+    assert O.rank_loads(C, 2).tolist() == [6, 6]
+    assert O.imbalance_max(O.rank_loads(C, 2)) == 1.0 and O.imbalance_max(C) == 2.0
+    assert O.rank_loads(C, 4).tolist() == [12] and O.imbalance_max(O.rank_loads(C, 4)) == 1.0
+    assert O.rank_loads(C, 1).tolist() == C.tolist()
+    rng = np.random.default_rng(2)
+    T, N, K = 50, 8, 2
+    z = rng.standard_normal((T, N))
+    idx = O.topk_select(z, K)
+    r = O.route_coefficients(z, idx, O.SOFTMAX, True, 1.0)
+    p = O.normalized_scores(z, O.SOFTMAX)
+    kept = O.keep_routes_rank_wide(idx, N, 4, 30)
+    st1 = O.balance_stats(p, idx, kept, r, N, group=1)
+    assert st1.imax_rank_req == st1.imax_req and st1.imax_rank_keep == st1.imax_keep
+    st = O.balance_stats(p, idx, kept, r, N, group=4)
+    Cq = O.rank_loads(O.requested_counts(idx, N), 4)
+    assert abs(st.imax_rank_req - 2 * Cq.max() / Cq.sum()) < 1e-15
+    assert math.isnan(O.balance_stats(p, idx, kept, r, N).imax_rank_req)
+    with pytest.raises(ValueError):
+        O.destination_of(6, 4)
