@@ -77,9 +77,16 @@ const char* moe_status_string(int status);
  * evaluated in double precision. Returns -1 when c < 0 (unlimited capacity). */
 int moe_capacity_from_factor(double c, int K, int T, int N);
 
-/* Host. Rows needed for packed per-expert buffers: min(K T, N capacity), or K T when
- * capacity < 0. Every kept route owns one row (Section 10 Eq. 26). */
-int moe_max_rows(int T, int N, int K, int capacity);
+/* Host. Rank-wide budget max(1, ceil(c * K * T_s)) of Section 10 Eq. 23: one limit
+ * shared by the experts of a destination, T_route = K T_s the routes of one source
+ * shard of T_s tokens. Double precision; -1 when c < 0 (unlimited). */
+int moe_rank_capacity_from_factor(double c, int K, int T_s);
+
+/* Host. Rows needed for packed per-expert buffers: every kept route owns one row
+ * (Section 10 Eq. 26), so min(K T, N capacity) under per-expert capacity
+ * (capacity_group = 0), min(K T, (N / capacity_group) capacity) under rank-wide
+ * capacity, and K T when capacity < 0. */
+int moe_max_rows(int T, int N, int K, int capacity, int capacity_group);
 
 /* ---------------------------------------------------------------------------------
  * moe_route: router logits, scores, top-K selection and routed coefficients, plus the
@@ -112,10 +119,16 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
               size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
- * moe_permute: requested counts, per-expert capacity admission, offsets, restoration
- * map and the packed rows (Section 10 Eq. 19, 21, 25, 26 and Section 10.3).
+ * moe_permute: requested counts, capacity admission, offsets, restoration map and the
+ * packed rows (Section 10 Eq. 19, 21, 23, 25, 26 and Section 10.3).
  *
- *   capacity           routes kept per expert (first come by token index), < 0 = all
+ *   capacity           < 0: every route is kept. capacity_group = 0: routes kept per
+ *                      expert, first come by token index (Eq. 25). capacity_group = g > 0:
+ *                      experts [q g, (q+1) g) form destination q and share one budget of
+ *                      `capacity` rows (Eq. 23), admitted local-expert-major with a
+ *                      token-order prefix per expert (the batch's tokens are the source
+ *                      shards in rank order); N must be a multiple of g, g = 1 is the
+ *                      per-expert limit
  *   x                  [T][d_model] (dtype dt)
  *   topk_idx           [T][K] int32 in (each row holds K distinct experts in [0, N))
  *   C_req, C_keep      [N] int32 out: requested and kept counts (M_i = C_keep[i])
@@ -127,14 +140,14 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
  *                      and beyond o_N are left untouched. May be NULL: then only the
  *                      counts and maps are written, and the grouped GEMM gathers its
  *                      rows from x through row_token instead (no packed copy in HBM)
- *   max_rows           >= moe_max_rows(T, N, K, capacity)
+ *   max_rows           >= moe_max_rows(T, N, K, capacity, capacity_group)
  *   workspace          moe_permute_workspace_size(T, N, K) bytes
  * ------------------------------------------------------------------------------- */
 size_t moe_permute_workspace_size(int T, int N, int K);
-int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const void* x,
-                const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep, int32_t* offsets,
-                int32_t* dest_row, int32_t* row_token, void* x_perm, int max_rows,
-                void* workspace, size_t workspace_bytes, hipStream_t stream);
+int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_group, int dt,
+                const void* x, const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep,
+                int32_t* offsets, int32_t* dest_row, int32_t* row_token, void* x_perm,
+                int max_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_grouped_swiglu: G SwiGLU experts over densely packed row segments, as a grouped
@@ -260,6 +273,9 @@ int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
  *   stats[MOE_STAT_DELTA_ROUTE]    (K T - sum C_keep) / (K T)                  (Eq. 27)
  *   stats[MOE_STAT_TOKENS_LOST_ANY|ALL] tokens with >= 1 / all K routes dropped (Sec. 10.3)
  *   stats[MOE_STAT_WEIGHT_REMOVED] dropped share of the selected coefficient mass sum r
+ *   stats[MOE_STAT_IMAX_RANK_REQ|KEEP] Eq. 22 on destination totals R_q (Eq. 20, 21) when
+ *                                  expert_group = g > 0 (destination q owns experts
+ *                                  [q g, (q+1) g)); NaN when expert_group = 0
  * Ratios of an all-zero count vector are NaN. Sums run in a fixed order (repeatable).
  *
  *   logits             [T][N] float32 router logits as moe_route writes them (bias added)
@@ -267,7 +283,8 @@ int moe_combine(int T, int d_model, int K, int dt, const void* f_perm,
  *   P                  [N] float32 out; stats [MOE_STAT_COUNT] float32 out
  *   workspace          moe_balance_stats_workspace_size(T, N) bytes
  * All buffers are device memory owned by the caller. Returns MOE_ERR_INVALID_ARG for
- * K > N, a non-positive size, an unknown score mode or a NULL buffer, MOE_ERR_UNSUPPORTED
+ * K > N, a non-positive size, an unknown score mode, a NULL buffer, a negative
+ * expert_group or one that does not divide N, MOE_ERR_UNSUPPORTED
  * for N > 256 or K > 16, MOE_ERR_WORKSPACE for a short workspace; T = 0 enqueues nothing.
  * ------------------------------------------------------------------------------- */
 enum moe_stat {
@@ -283,13 +300,15 @@ enum moe_stat {
   MOE_STAT_TOKENS_LOST_ANY = 9,
   MOE_STAT_TOKENS_LOST_ALL = 10,
   MOE_STAT_WEIGHT_REMOVED = 11,
-  MOE_STAT_COUNT = 12
+  MOE_STAT_IMAX_RANK_REQ = 12,
+  MOE_STAT_IMAX_RANK_KEEP = 13,
+  MOE_STAT_COUNT = 14
 };
 size_t moe_balance_stats_workspace_size(int T, int N);
-int moe_balance_stats(int T, int N, int K, int score, const float* logits, const int32_t* C_req,
-                      const int32_t* C_keep, const int32_t* dest_row, const float* topk_r,
-                      float* P, float* stats, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream);
+int moe_balance_stats(int T, int N, int K, int score, int expert_group, const float* logits,
+                      const int32_t* C_req, const int32_t* C_keep, const int32_t* dest_row,
+                      const float* topk_r, float* P, float* stats, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_forward: the whole layer: route -> permute -> grouped SwiGLU experts -> shared
@@ -303,7 +322,9 @@ typedef struct moe_forward_args {
   int score, renorm;     /* moe_score, 0/1 */
   float alpha;           /* routed scale */
   float s;               /* shared gain when w_shared_gate == NULL */
-  int capacity;          /* routes kept per expert, < 0 = unlimited */
+  int capacity;          /* < 0 = unlimited; per expert, or per destination group */
+  int capacity_group;    /* 0: per-expert capacity; g > 0: rank-wide budget shared by each
+                            group of g consecutive experts (as in moe_permute) */
   int dt;                /* moe_dtype */
   int weights_packed;    /* 1: w_gate/w_up/w_down and ws_* are in the moe_pack_weights
                             layout (bf16; the fast path), 0: row-major */
@@ -320,7 +341,7 @@ typedef struct moe_forward_args {
   void* y;               /* [T][d_model] out */
   /* Optional outputs: when non-NULL the intermediate is written there, otherwise it
    * lives in the workspace. Shapes as in the per-stage entry points; `rows` below is
-   * moe_max_rows(T, N, K, capacity). */
+   * moe_max_rows(T, N, K, capacity, capacity_group). */
   float* logits;         /* [T][N] */
   int32_t* topk_idx;     /* [T][K] */
   float* topk_r;         /* [T][K] */
@@ -335,8 +356,9 @@ typedef struct moe_forward_args {
   void* h_perm;          /* [rows][d_r] */
   void* f_perm;          /* [rows][d_model] */
   void* g;               /* [T][d_model] shared output */
-  /* Balance statistics (moe_balance_stats) of the same batch, computed after the combine
-   * when both are non-NULL (one without the other is MOE_ERR_INVALID_ARG): */
+  /* Balance statistics (moe_balance_stats, expert_group = capacity_group) of the same
+   * batch, computed after the combine when both are non-NULL (one without the other is
+   * MOE_ERR_INVALID_ARG): */
   float* balance_P;      /* [N] */
   float* balance_stats;  /* [MOE_STAT_COUNT] */
 } moe_forward_args;

@@ -34,6 +34,13 @@ int check_router_dims(int T, int d_model, int N, int K) {
   return MOE_OK;
 }
 
+// experts per destination group: 0 = none, else a divisor of N (every destination owns
+// the same number of experts)
+int check_group(int N, int group) {
+  if (group < 0 || (group > 0 && N % group != 0)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 int check_dtype(int dt) { return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_INVALID_ARG; }
 
 size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
@@ -82,7 +89,8 @@ size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
   Carver c(ws);
   FwdWs w;
   const size_t T = a->T, K = a->K, N = a->N, d = a->d_model;
-  const size_t rows = static_cast<size_t>(moe_max_rows(a->T, a->N, a->K, a->capacity));
+  const size_t rows =
+      static_cast<size_t>(moe_max_rows(a->T, a->N, a->K, a->capacity, a->capacity_group));
   const size_t es = esize(a->dt);
   const bool gate = a->w_shared_gate != nullptr;
   w.topk_idx = a->topk_idx ? a->topk_idx : c.take<int32_t>(T * K);
@@ -133,11 +141,19 @@ int moe_capacity_from_factor(double c, int K, int T, int N) {
   return v >= static_cast<double>(INT_MAX) ? INT_MAX : static_cast<int>(v);
 }
 
-int moe_max_rows(int T, int N, int K, int capacity) {
+int moe_rank_capacity_from_factor(double c, int K, int T_s) {
+  if (c < 0.0) return -1;
+  const double v = std::ceil(c * K * T_s);
+  if (v < 1.0) return 1;
+  return v >= static_cast<double>(INT_MAX) ? INT_MAX : static_cast<int>(v);
+}
+
+int moe_max_rows(int T, int N, int K, int capacity, int capacity_group) {
   const long kt = static_cast<long>(K) * (T > 0 ? T : 0);
   long r = kt;
   if (capacity >= 0) {
-    const long nc = static_cast<long>(N) * capacity;
+    const long budgets = capacity_group > 0 ? N / capacity_group : N;
+    const long nc = budgets * capacity;
     r = nc < kt ? nc : kt;
   }
   return r > INT_MAX ? INT_MAX : static_cast<int>(r);
@@ -173,7 +189,7 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
                        topk_idx, topk_r, s_tok, stream));
   if (C_req) {
     MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-    MOE_HIP(launch_scan(T, N, -1, w.hist, C_req, w.c_keep, w.offsets, stream));
+    MOE_HIP(launch_scan(T, N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, stream));
   }
   return MOE_OK;
 }
@@ -183,21 +199,22 @@ size_t moe_permute_workspace_size(int T, int N, int K) {
   return carve_count(nullptr, T, N, K, false, nullptr);
 }
 
-int moe_permute(int T, int d_model, int N, int K, int capacity, int dt, const void* x,
-                const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep, int32_t* offsets,
-                int32_t* dest_row, int32_t* row_token, void* x_perm, int max_rows,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_group, int dt,
+                const void* x, const int32_t* topk_idx, int32_t* C_req, int32_t* C_keep,
+                int32_t* offsets, int32_t* dest_row, int32_t* row_token, void* x_perm,
+                int max_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_router_dims(T, d_model, N, K));
   MOE_TRY(check_dtype(dt));
+  MOE_TRY(check_group(N, capacity_group));
   if (!x || !topk_idx || !C_req || !C_keep || !offsets || !dest_row || !row_token)
     return MOE_ERR_INVALID_ARG;
-  if (max_rows < moe_max_rows(T, N, K, capacity)) return MOE_ERR_INVALID_ARG;
+  if (max_rows < moe_max_rows(T, N, K, capacity, capacity_group)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_permute_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
   CountWs w{};
   carve_count(workspace, T, N, K, false, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, capacity, w.hist, C_req, C_keep, offsets, stream));
+  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, stream));
   MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
                          dest_row, row_token, x_perm, stream));
   return MOE_OK;
@@ -379,11 +396,12 @@ size_t moe_balance_stats_workspace_size(int T, int N) {
   return stats_workspace_bytes(T, N);
 }
 
-int moe_balance_stats(int T, int N, int K, int score, const float* logits, const int32_t* C_req,
-                      const int32_t* C_keep, const int32_t* dest_row, const float* topk_r,
-                      float* P, float* stats, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+int moe_balance_stats(int T, int N, int K, int score, int expert_group, const float* logits,
+                      const int32_t* C_req, const int32_t* C_keep, const int32_t* dest_row,
+                      const float* topk_r, float* P, float* stats, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || N <= 0 || K <= 0 || K > N) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_group(N, expert_group));
   if (N > moe::kMaxN || K > moe::kMaxK) return MOE_ERR_UNSUPPORTED;
   if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
   if (!logits || !C_req || !C_keep || !dest_row || !topk_r || !P || !stats)
@@ -391,8 +409,8 @@ int moe_balance_stats(int T, int N, int K, int score, const float* logits, const
   if (T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_balance_stats_workspace_size(T, N))
     return MOE_ERR_WORKSPACE;
-  MOE_HIP(launch_balance_stats(T, N, K, score, logits, dest_row, topk_r, C_req, C_keep, P, stats,
-                               workspace, stream));
+  MOE_HIP(launch_balance_stats(T, N, K, score, expert_group, logits, dest_row, topk_r, C_req,
+                               C_keep, P, stats, workspace, stream));
   return MOE_OK;
 }
 
@@ -416,17 +434,19 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   if (a->weights_packed != 0 && a->weights_packed != 1) return MOE_ERR_INVALID_ARG;
   if (a->weights_packed && a->dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if ((a->balance_P == nullptr) != (a->balance_stats == nullptr)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_group(a->N, a->capacity_group));
   if (a->T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_forward_workspace_size(a)) return MOE_ERR_WORKSPACE;
   FwdWs w{};
   carve_forward(a, workspace, &w);
   const int T = a->T, d = a->d_model, N = a->N, K = a->K;
-  const int rows = moe_max_rows(T, N, K, a->capacity);
+  const int rows = moe_max_rows(T, N, K, a->capacity, a->capacity_group);
   MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
                        a->logit_bias, a->w_shared_gate, w.logits, 0, w.topk_idx, w.topk_r,
                        w.s_tok, stream));
   MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, a->capacity, w.hist, w.C_req, w.C_keep, w.offsets, stream));
+  MOE_HIP(launch_scan(T, N, a->capacity, a->capacity_group, w.hist, w.C_req, w.C_keep,
+                      w.offsets, stream));
   MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
   MOE_HIP(expert_passes(N, d, a->d_r, a->d_s, a->dt, a->weights_packed == 1, a->x, T,
@@ -435,8 +455,9 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   MOE_HIP(launch_combine(T, d, K, a->dt, w.f_perm, w.dest_row, w.topk_r, w.g, a->s, w.s_tok,
                          a->y, stream));
   if (w.stats_ws != nullptr)
-    MOE_HIP(launch_balance_stats(T, N, K, a->score, w.logits, w.dest_row, w.topk_r, w.C_req,
-                                 w.C_keep, a->balance_P, a->balance_stats, w.stats_ws, stream));
+    MOE_HIP(launch_balance_stats(T, N, K, a->score, a->capacity_group, w.logits, w.dest_row,
+                                 w.topk_r, w.C_req, w.C_keep, a->balance_P, a->balance_stats,
+                                 w.stats_ws, stream));
   return MOE_OK;
 }
 

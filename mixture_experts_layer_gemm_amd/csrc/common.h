@@ -63,7 +63,9 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
 hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
                         int32_t* loc_rank, hipStream_t stream);
 
-hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
+// capacity < 0: keep every route; group == 0: per-expert limit; group > 0: one budget
+// `capacity` shared by each run of `group` consecutive experts
+hipError_t launch_scan(int T, int N, int capacity, int group, int32_t* hist, int32_t* C_req,
                        int32_t* C_keep, int32_t* offsets, hipStream_t stream);
 
 // x_perm == nullptr: restoration map only (no row copy)
@@ -74,7 +76,7 @@ hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* 
                           void* x_perm, hipStream_t stream);
 
 size_t stats_workspace_bytes(int T, int N);
-hipError_t launch_balance_stats(int T, int N, int K, int score, const float* logits,
+hipError_t launch_balance_stats(int T, int N, int K, int score, int group, const float* logits,
                                 const int32_t* dest_row, const float* topk_r,
                                 const int32_t* C_req, const int32_t* C_keep, float* P,
                                 float* stats, void* workspace, hipStream_t stream);

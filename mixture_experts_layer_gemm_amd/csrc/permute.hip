@@ -1,17 +1,23 @@
-// Requested counts, per-expert capacity admission, offsets and the packed row copy.
+// Requested counts, capacity admission, offsets and the packed row copy.
 //
 // Follows "Section 10: Routing, Capacity, and Load Balancing": requested counts
-// (Eq. 19), kept counts M_i and drops (Eq. 21), the independent per-expert capacity
-// (Eq. 25) admitting routes first come by token index, and the real-count offsets
-// o_j = sum_{i<=j} M_i of the densely packed expert segments (Eq. 26).
+// (Eq. 19), kept counts M_i and drops (Eq. 21), and the real-count offsets
+// o_j = sum_{i<=j} M_i of the densely packed expert segments (Eq. 26). Two capacity
+// policies: the independent per-expert limit (Eq. 25), admitting routes first come by
+// token index, and the rank-wide budget of Eq. 23 / Section 10.3, shared by each group
+// of `group` consecutive experts (a destination). The rank-wide admission order is
+// local-expert-major, then source rank, with a prefix of each split kept; the batch's
+// sources are contiguous token shards in rank order, so that order is (expert, token)
+// and expert e keeps M_e = clamp(B - sum_{e' < e in its group} C_e'^req, 0, C_e^req):
+// either way the kept routes of an expert are its first M_e routes in token order.
 //
 // Deterministic by construction: no atomic decides a position.
 //   count   one wave per 64-token chunk: each expert's 64-bit token mask is built with
 //           LDS OR (order-free), so a route's rank inside the chunk is a popcount of
 //           the mask below its lane and the chunk histogram is the mask's popcount.
 //   scan    one workgroup: per-expert running sums over chunks, split over up to 1024
-//           threads (chunk base ranks and C^req), C^keep = min(C^req, capacity), and an
-//           exclusive scan over experts -> offsets.
+//           threads (chunk base ranks and C^req), C^keep from the capacity policy, and
+//           an exclusive scan over experts -> offsets.
 //   scatter one wave per token: rank = chunk base + rank in chunk; kept iff rank <
 //           C^keep; the token's row is read once (16-byte lanes, coalesced) and written
 //           to each kept destination.
@@ -63,10 +69,11 @@ constexpr int SCAN_THREADS = 1024;
 // (NP = N rounded up to a power of two): its loads are independent and coalesced
 // across the experts; a scan over the P runs of each expert then gives the bases.
 __global__ void __launch_bounds__(SCAN_THREADS)
-scan_kernel(int nchunks, int N, int NP, int capacity, int32_t* __restrict__ hist,
+scan_kernel(int nchunks, int N, int NP, int capacity, int group, int32_t* __restrict__ hist,
             int32_t* __restrict__ C_req, int32_t* __restrict__ C_keep,
             int32_t* __restrict__ offsets) {
   __shared__ int32_t part[SCAN_THREADS];
+  __shared__ int32_t req[kMaxN];
   __shared__ int32_t keep[kMaxN];
   const int tid = threadIdx.x;
   const int P = SCAN_THREADS / NP;
@@ -112,10 +119,25 @@ scan_kernel(int nchunks, int N, int NP, int capacity, int32_t* __restrict__ hist
     }
     if (p == P - 1) {
       C_req[e] = run;
-      const int kk = (capacity < 0 || run < capacity) ? run : capacity;
-      C_keep[e] = kk;
-      keep[e] = kk;
+      req[e] = run;
     }
+  }
+  __syncthreads();
+  // kept counts (thread tid owns expert tid)
+  if (tid < N) {
+    const int r = req[tid];
+    int kk = r;
+    if (capacity >= 0) {
+      if (group > 0) {  // shared destination budget, earlier local experts first
+        int before = 0;
+        for (int q = tid - tid % group; q < tid; ++q) before += req[q];
+        kk = min(r, max(capacity - before, 0));
+      } else {
+        kk = min(r, capacity);
+      }
+    }
+    C_keep[tid] = kk;
+    keep[tid] = kk;
   }
   __syncthreads();
   // exclusive scan of C_keep over experts (N <= 256): Hillis-Steele in part[0..N)
@@ -205,13 +227,13 @@ hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* h
   return hipGetLastError();
 }
 
-hipError_t launch_scan(int T, int N, int capacity, int32_t* hist, int32_t* C_req,
+hipError_t launch_scan(int T, int N, int capacity, int group, int32_t* hist, int32_t* C_req,
                        int32_t* C_keep, int32_t* offsets, hipStream_t stream) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   int NP = 1;
   while (NP < N) NP <<= 1;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, nchunks, N, NP,
-                     capacity, hist, C_req, C_keep, offsets);
+                     capacity, group, hist, C_req, C_keep, offsets);
   return hipGetLastError();
 }
 

@@ -5,7 +5,9 @@
 // scalar N f.P (Eq. 30), max/mean imbalance (Eq. 22, 39), normalized entropy deficit,
 // coefficient of variation and never-selected count (Section 10.2), the route-drop
 // fraction (Eq. 27) and the per-token drop measures Section 10.3 asks for (tokens losing
-// at least one and all K routes, selected coefficient mass removed).
+// at least one and all K routes, selected coefficient mass removed). With destination
+// groups of g consecutive experts, also max/mean imbalance of the requested and kept
+// destination totals (Eq. 20-22).
 //
 // stats_partial_kernel: one wave per token, 4 waves per workgroup, TPB tokens per
 // workgroup. A wave normalizes its token's N scores (full softmax of the logits, or
@@ -153,11 +155,12 @@ __device__ double sf_max(double v, double* red) {
 }
 
 __global__ void __launch_bounds__(SF_THREADS)
-stats_final_kernel(int T, int N, int K, int nblk, const float* __restrict__ colsum,
+stats_final_kernel(int T, int N, int K, int group, int nblk, const float* __restrict__ colsum,
                    const float* __restrict__ drops, const int32_t* __restrict__ C_req,
                    const int32_t* __restrict__ C_keep, float* __restrict__ P_out,
                    float* __restrict__ stats) {
   __shared__ double red[SF_THREADS];
+  __shared__ double s_req[SF_THREADS], s_keep[SF_THREADS];
   const int tid = threadIdx.x;
   const double KT = static_cast<double>(K) * T;
   // P_i and per-expert terms (N <= 256: one expert per thread)
@@ -181,6 +184,18 @@ stats_final_kernel(int T, int N, int K, int nblk, const float* __restrict__ cols
   const double mean_req = sreq / N, mean_keep = skeep / N;
   const double vreq = sf_sum(act ? (creq - mean_req) * (creq - mean_req) : 0.0, red) / N;
   const double vkeep = sf_sum(act ? (ckeep - mean_keep) * (ckeep - mean_keep) : 0.0, red) / N;
+  // destination totals R_q (thread q < N / group sums its group's experts in order)
+  s_req[tid] = creq;
+  s_keep[tid] = ckeep;
+  __syncthreads();
+  const int M = group > 0 ? N / group : 0;
+  double rreq = 0.0, rkeep = 0.0;
+  if (tid < M)
+    for (int j = tid * group; j < (tid + 1) * group; ++j) {
+      rreq += s_req[j];
+      rkeep += s_keep[j];
+    }
+  const double mrreq = sf_max(rreq, red), mrkeep = sf_max(rkeep, red);
   // drop partials, in workgroup order
   double d[4] = {0.0, 0.0, 0.0, 0.0};
   if (tid < 4)
@@ -203,6 +218,9 @@ stats_final_kernel(int T, int N, int K, int nblk, const float* __restrict__ cols
     stats[MOE_STAT_TOKENS_LOST_ANY] = static_cast<float>(red[0]);
     stats[MOE_STAT_TOKENS_LOST_ALL] = static_cast<float>(red[1]);
     stats[MOE_STAT_WEIGHT_REMOVED] = static_cast<float>(red[3] > 0 ? red[2] / red[3] : nan);
+    // destination totals sum to the expert totals
+    stats[MOE_STAT_IMAX_RANK_REQ] = static_cast<float>(M > 0 && sreq > 0 ? M * mrreq / sreq : nan);
+    stats[MOE_STAT_IMAX_RANK_KEEP] = static_cast<float>(M > 0 && skeep > 0 ? M * mrkeep / skeep : nan);
   }
 }
 
@@ -213,7 +231,7 @@ size_t stats_workspace_bytes(int T, int N) {
   return nblk * (static_cast<size_t>(N) + 4) * sizeof(float);
 }
 
-hipError_t launch_balance_stats(int T, int N, int K, int score, const float* logits,
+hipError_t launch_balance_stats(int T, int N, int K, int score, int group, const float* logits,
                                 const int32_t* dest_row, const float* topk_r,
                                 const int32_t* C_req, const int32_t* C_keep, float* P,
                                 float* stats, void* workspace, hipStream_t stream) {
@@ -222,7 +240,7 @@ hipError_t launch_balance_stats(int T, int N, int K, int score, const float* log
   float* drops = colsum + static_cast<size_t>(nblk) * N;
   hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(ST_WAVES * kWave), 0, stream, T, N,
                      K, score, logits, dest_row, topk_r, colsum, drops);
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(SF_THREADS), 0, stream, T, N, K, nblk,
-                     colsum, drops, C_req, C_keep, P, stats);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(SF_THREADS), 0, stream, T, N, K, group,
+                     nblk, colsum, drops, C_req, C_keep, P, stats);
   return hipGetLastError();
 }

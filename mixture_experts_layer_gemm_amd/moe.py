@@ -32,7 +32,8 @@ class MoEError(RuntimeError):
 class ForwardArgs(ctypes.Structure):
     """Mirror of moe_forward_args."""
     _fields_ = [(n, c_int) for n in ("T", "d_model", "N", "K", "d_r", "d_s", "score", "renorm")] + [
-        ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("dt", c_int),
+        ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("capacity_group", c_int),
+        ("dt", c_int),
         ("weights_packed", c_int)] + [
         (n, c_void_p) for n in ("x", "w_router", "logit_bias", "w_shared_gate", "w_gate", "w_up",
                                 "w_down", "ws_gate", "ws_up", "ws_down", "y", "logits", "topk_idx",
@@ -43,7 +44,7 @@ class ForwardArgs(ctypes.Structure):
 # order of moe_balance_stats' output vector (enum moe_stat)
 STAT_NAMES = ["lbl", "imax_req", "imax_keep", "ih_req", "ih_keep", "cv_req", "cv_keep",
               "never_selected", "delta_route", "tokens_lost_any", "tokens_lost_all",
-              "weight_removed"]
+              "weight_removed", "imax_rank_req", "imax_rank_keep"]
 
 
 def _load() -> ctypes.CDLL:
@@ -55,18 +56,19 @@ def _load() -> ctypes.CDLL:
     sig = {
         "moe_status_string": (ctypes.c_char_p, [I]),
         "moe_capacity_from_factor": (I, [c_double, I, I, I]),
-        "moe_max_rows": (I, [I, I, I, I]),
+        "moe_rank_capacity_from_factor": (I, [c_double, I, I]),
+        "moe_max_rows": (I, [I, I, I, I, I]),
         "moe_route_workspace_size": (S, [I, I, I]),
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
-        "moe_permute": (I, [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
+        "moe_permute": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
         "moe_grouped_swiglu": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P]),
         "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P]),
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
         "moe_combine": (I, [I, I, I, I, P, P, P, P, F, P, P, P]),
         "moe_experts": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, I, P]),
         "moe_balance_stats_workspace_size": (S, [I, I]),
-        "moe_balance_stats": (I, [I, I, I, I, P, P, P, P, P, P, P, P, S, P]),
+        "moe_balance_stats": (I, [I, I, I, I, I, P, P, P, P, P, P, P, P, S, P]),
         "moe_forward_workspace_size": (S, [POINTER(ForwardArgs)]),
         "moe_forward": (I, [POINTER(ForwardArgs), P, S, P]),
     }
@@ -96,8 +98,12 @@ def capacity_from_factor(c: float, K: int, T: int, N: int) -> int:
     return lib.moe_capacity_from_factor(float(c), K, T, N)
 
 
-def max_rows(T: int, N: int, K: int, capacity: int) -> int:
-    return lib.moe_max_rows(T, N, K, capacity)
+def rank_capacity_from_factor(c: float, K: int, T_s: int) -> int:
+    return lib.moe_rank_capacity_from_factor(float(c), K, T_s)
+
+
+def max_rows(T: int, N: int, K: int, capacity: int, capacity_group: int = 0) -> int:
+    return lib.moe_max_rows(T, N, K, capacity, capacity_group)
 
 
 # ---------------------------------------------------------------------------------------
@@ -163,13 +169,15 @@ def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = Tr
     return out
 
 
-def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True):
+def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True,
+                capacity_group: int = 0):
     """Counts, capacity admission, offsets, restoration map and (copy_rows) the packed
-    rows x_perm; without copy_rows the grouped GEMM gathers rows through row_token."""
+    rows x_perm; without copy_rows the grouped GEMM gathers rows through row_token.
+    capacity_group = g > 0 shares one budget `capacity` among each g consecutive experts."""
     T, d = x.shape
     K = topk_idx.shape[1]
     dev = x.device
-    rows = max_rows(T, N, K, capacity)
+    rows = max_rows(T, N, K, capacity, capacity_group)
     out = dict(C_req=torch.empty(N, dtype=torch.int32, device=dev),
                C_keep=torch.empty(N, dtype=torch.int32, device=dev),
                offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
@@ -178,7 +186,7 @@ def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True)
                x_perm=(torch.empty(max(rows, 1), d, dtype=x.dtype, device=dev)
                        if copy_rows else None))
     ws = _workspace(lib.moe_permute_workspace_size(T, N, K), dev)
-    st = lib.moe_permute(T, d, N, K, capacity, _dt(x), _ptr(x), _ptr(topk_idx),
+    st = lib.moe_permute(T, d, N, K, capacity, capacity_group, _dt(x), _ptr(x), _ptr(topk_idx),
                          _ptr(out["C_req"]), _ptr(out["C_keep"]), _ptr(out["offsets"]),
                          _ptr(out["dest_row"]), _ptr(out["row_token"]), _ptr(out["x_perm"]),
                          max(rows, 1), _ptr(ws), ws.numel(), _stream())
@@ -254,7 +262,8 @@ def moe_experts(x, row_token, offsets, max_rows: int, w_gate, w_up, w_down, shar
     return out
 
 
-def moe_balance_stats(logits, C_req, C_keep, dest_row, topk_r, score: int = SCORE_SOFTMAX):
+def moe_balance_stats(logits, C_req, C_keep, dest_row, topk_r, score: int = SCORE_SOFTMAX,
+                      expert_group: int = 0):
     """Balance statistics and drop diagnostics of one routed batch: returns (P, stats)
     with P the [N] mean normalized scores and stats a dict keyed by STAT_NAMES (device
     tensors; read them after the stream synchronizes)."""
@@ -264,7 +273,8 @@ def moe_balance_stats(logits, C_req, C_keep, dest_row, topk_r, score: int = SCOR
     P = torch.empty(N, dtype=torch.float32, device=dev)
     st = torch.empty(len(STAT_NAMES), dtype=torch.float32, device=dev)
     ws = _workspace(lib.moe_balance_stats_workspace_size(T, N), dev)
-    rc = lib.moe_balance_stats(T, N, K, score, _ptr(logits), _ptr(C_req), _ptr(C_keep),
+    rc = lib.moe_balance_stats(T, N, K, score, expert_group, _ptr(logits), _ptr(C_req),
+                               _ptr(C_keep),
                                _ptr(dest_row), _ptr(topk_r), _ptr(P), _ptr(st), _ptr(ws),
                                ws.numel(), _stream())
     _check("moe_balance_stats", rc)
@@ -304,7 +314,7 @@ class MoELayer:
 
     def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
-                 logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
+                 capacity_group: int = 0, logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
                  pack_weights=None, keep_x_perm=False, balance_stats=False):
         self.x = x
         T, d = x.shape
@@ -323,11 +333,12 @@ class MoELayer:
         self.shared_mlp = shared_mlp      # (gate, up, down) of the one shared MLP, or None
         d_s = shared_mlp[0].shape[0] if shared_mlp else 0
         self.y = torch.empty(T, d, dtype=x.dtype, device=dev)
-        self.rows = max_rows(T, N, K, capacity)
+        self.rows = max_rows(T, N, K, capacity, capacity_group)
         self.out = {}
         a = ForwardArgs()
         a.T, a.d_model, a.N, a.K, a.d_r, a.d_s = T, d, N, K, d_r, d_s
         a.score, a.renorm, a.alpha, a.s, a.capacity, a.dt = score, int(renorm), alpha, s, capacity, _dt(x)
+        a.capacity_group = capacity_group
         a.weights_packed = int(self.weights_packed)
         a.x, a.w_router, a.w_gate, a.w_up, a.w_down = (_ptr(x), _ptr(w_router), _ptr(w_gate),
                                                        _ptr(w_up), _ptr(w_down))

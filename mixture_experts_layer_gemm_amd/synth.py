@@ -47,6 +47,7 @@ class Config:
     alpha: float = 1.0
     s: float = 1.0
     capacity_factor: Optional[float] = None      # None = unlimited (dropless)
+    capacity_group: int = 0                      # > 0: rank-wide budget per group of experts
     dtype: str = "bf16"                          # "bf16" or "f32"
     std_x: float = 1.0
     std_w: float = 0.02
@@ -118,6 +119,15 @@ SMALL = {
     "S_stream_cap": Config("small-stream-capacity-gate", 20, T=2048, d_model=512, N=16, K=4,
                            d_r=512, shared_widths=(256, 256), renorm=False, alpha=1.0,
                            capacity_factor=1.0, zipf_bias=True, shared_gate=True, std_w=0.04),
+    # rank-wide capacity: four destinations of four experts share one budget each
+    "S_rankcap": Config("small-rank-capacity", 21, T=600, d_model=256, N=16, K=4, d_r=192,
+                        shared_widths=(128,), alpha=4.0, capacity_factor=1.0, capacity_group=4,
+                        zipf_bias=True, std_w=0.05),
+    # tighter rank-wide budget on the persistent-GEMM shapes, sigmoid routing
+    "S_rankcap_stream": Config("small-stream-rank-capacity", 22, T=2048, d_model=512, N=16,
+                               K=4, d_r=512, shared_widths=(256,), score=SCORE_SIGMOID,
+                               alpha=2.5, capacity_factor=0.75, capacity_group=2,
+                               zipf_bias=True, std_w=0.04),
 }
 
 

@@ -429,7 +429,8 @@ class LayerSpec:
     renorm: bool = True
     alpha: float = 1.0
     s: float = 1.0                    # fixed shared gain when there is no learned gate
-    capacity: int = -1                # routes kept per expert; < 0 = unlimited
+    capacity: int = -1                # routes kept per expert (or per destination); < 0 = unlimited
+    capacity_group: int = 0           # > 0: destinations of this many experts share `capacity`
 
 
 @dataclass
@@ -464,7 +465,11 @@ def forward(spec: LayerSpec, x, w_router, expert_weights: Callable[[int], tuple]
     r = route_coefficients(keys, idx, spec.score, spec.renorm, spec.alpha)
     s_tok = shared_gate(x, w_shared_gate) if w_shared_gate is not None else None
     C_req = requested_counts(idx, spec.N)
-    kept = keep_routes(idx, spec.N, spec.capacity)
+    if spec.capacity_group > 0:
+        kept = keep_routes_rank_wide(idx, spec.N, spec.capacity_group, spec.capacity,
+                                     n_sources=spec.N // spec.capacity_group)
+    else:
+        kept = keep_routes(idx, spec.N, spec.capacity)
     perm = permutation(idx, kept, spec.N)
     R = int(perm.offsets[-1])
     d = x.shape[1]

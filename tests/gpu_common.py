@@ -49,6 +49,18 @@ def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+def layer_capacity(cfg: synth.Config, T: int) -> int:
+    """Capacity of a config: unlimited, the per-expert limit of Eq. 25, or the rank-wide
+    budget of Eq. 23 with the batch split into as many equal source shards as there are
+    destinations (T_s = ceil(T / M_E))."""
+    if cfg.capacity_factor is None:
+        return -1
+    if cfg.capacity_group > 0:
+        M_E = cfg.N // cfg.capacity_group
+        return O.rank_capacity_from_factor(cfg.capacity_factor, cfg.K, -(-T // M_E))
+    return O.capacity_from_factor(cfg.capacity_factor, cfg.K, T, cfg.N)
+
+
 class DeviceLayer:
     """A config's seeded inputs on the host (stored bits) and on the device."""
 
@@ -67,13 +79,20 @@ class DeviceLayer:
         self.shared = [tuple(to_device(w, dt) for w in s) for s in inp.shared]
         self.bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).cuda()
         self.gate = None if inp.w_shared_gate is None else to_device(inp.w_shared_gate, dt)
-        self.capacity = (-1 if cfg.capacity_factor is None else
-                         O.capacity_from_factor(cfg.capacity_factor, cfg.K, self.T, cfg.N))
+        self.capacity = layer_capacity(cfg, self.T)
 
     def spec(self) -> O.LayerSpec:
         c = self.cfg
         return O.LayerSpec(N=c.N, K=c.K, score=c.score, renorm=c.renorm, alpha=c.alpha, s=c.s,
-                           capacity=self.capacity)
+                           capacity=self.capacity, capacity_group=c.capacity_group)
+
+    def keep(self, idx):
+        """The oracle's kept-route mask for this layer's capacity policy."""
+        c = self.cfg
+        if c.capacity_group > 0:
+            return O.keep_routes_rank_wide(idx, c.N, c.capacity_group, self.capacity,
+                                           n_sources=c.N // c.capacity_group)
+        return O.keep_routes(idx, c.N, self.capacity)
 
     def x_f(self):
         return self.inp.as_float(self.inp.x)
@@ -81,6 +100,7 @@ class DeviceLayer:
     def layer_kwargs(self):
         c = self.cfg
         return dict(score=c.score, renorm=c.renorm, alpha=c.alpha, s=c.s, capacity=self.capacity,
+                    capacity_group=c.capacity_group,
                     logit_bias=self.bias, w_shared_gate=self.gate,
                     shared=self.shared if self.shared else None)
 

@@ -13,7 +13,7 @@ EXPECTED = ["moe_balance_stats", "moe_balance_stats_workspace_size",
             "moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
             "moe_forward_workspace_size",
             "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_pack_weights", "moe_permute",
-            "moe_permute_workspace_size",
+            "moe_permute_workspace_size", "moe_rank_capacity_from_factor",
             "moe_route", "moe_route_workspace_size", "moe_status_string"]
 
 
@@ -45,6 +45,16 @@ def test_capacity_unlimited_and_max_rows():
     assert moe.max_rows(4096, 64, 4, 256) == 64 * 256
     assert moe.max_rows(4096, 64, 4, 10) == 640
     assert moe.max_rows(100, 64, 4, 0) == 0
+    assert moe.max_rows(4096, 64, 4, 2000, 8) == 8 * 2000      # eight shared budgets
+    assert moe.max_rows(4096, 64, 4, 5000, 16) == 4 * 4096     # capped by K T
+    assert moe.max_rows(4096, 64, 4, 300, 1) == moe.max_rows(4096, 64, 4, 300)
+
+
+@pytest.mark.parametrize("c,K,T_s", [(1.0, 4, 1000), (1.25, 4, 1001), (0.0, 4, 10), (1e-6, 1, 10),
+                                     (2.0, 8, 512)])
+def test_rank_capacity_matches_eq23(c, K, T_s):
+    assert moe.rank_capacity_from_factor(c, K, T_s) == O.rank_capacity_from_factor(c, K, T_s)
+    assert moe.rank_capacity_from_factor(-1.0, K, T_s) == -1
 
 
 def test_workspace_sizes_are_positive_and_monotone():
@@ -90,11 +100,17 @@ def test_route_rejects_bad_arguments_without_launching():
 
 def test_permute_grouped_combine_forward_reject_bad_arguments():
     L = moe.lib
-    assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 31, 1, 1 << 20, None) == \
+    assert L.moe_permute(16, 64, 8, 2, -1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 31, 1, 1 << 20, None) == \
         moe.MOE_ERR_INVALID_ARG                               # max_rows < K T
-    assert L.moe_permute(16, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, None, 0, None) == \
+    assert L.moe_permute(16, 64, 8, 2, -1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, None, 0, None) == \
         moe.MOE_ERR_WORKSPACE
-    assert L.moe_permute(0, 64, 8, 2, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, None, 0, None) == moe.MOE_OK
+    assert L.moe_permute(0, 64, 8, 2, -1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, None, 0, None) == moe.MOE_OK
+    assert L.moe_permute(16, 64, 8, 2, 4, 3, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, 1, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG                               # 3 experts per group: 8 % 3 != 0
+    assert L.moe_permute(16, 64, 8, 2, 4, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 32, 1, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(16, 64, 8, 2, 4, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1, 7, 1, 1 << 20, None) == \
+        moe.MOE_ERR_INVALID_ARG                               # 2 groups x 4 rows > 7
     assert L.moe_grouped_swiglu(2, 64, 100, 1, 0, 1, 0, None, 1, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_grouped_swiglu(2, 64, 128, 1, 0, 1, 0, None, None, 8, 1, 1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_grouped_swiglu(1, 64, 128, 1, 0, 1, 0, None, None, 0, 1, 1, 1, 1, 1, None) == moe.MOE_OK
@@ -103,11 +119,12 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 1, 1, 0, 1, None, 8, 1, 1, 1, None) == \
         moe.MOE_ERR_INVALID_ARG                               # row index needs a_rows
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
-    bs = [64, 8, 2, 0, 1, 1, 1, 1, 1, 1, 1]
+    bs = [64, 8, 2, 0, 0, 1, 1, 1, 1, 1, 1, 1]
     assert L.moe_balance_stats(*bs, None, 0, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_balance_stats(64, 8, 9, *bs[3:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG  # K > N
     assert L.moe_balance_stats(64, 300, 2, *bs[3:], 1, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_balance_stats(*bs[:4], None, *bs[5:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_stats(*bs[:5], None, *bs[6:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_balance_stats(*bs[:4], 3, *bs[5:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_balance_stats(0, *bs[1:], None, 0, None) == moe.MOE_OK
     assert moe.lib.moe_balance_stats_workspace_size(4096, 64) >= 64 * 64 * 4
     ex = [8, 512, 512, 512, 1, 1, 1, 64, 1, 1, 64, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1]
@@ -135,6 +152,8 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     args.K, args.T = 2, 0
     assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_OK
     args.balance_P = 1                                        # P without the stats vector
+    assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    args.balance_P, args.capacity_group = None, 3             # 8 experts in groups of 3
     assert L.moe_forward(ctypes.byref(args), None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 

@@ -29,7 +29,7 @@ def setup_module(module):
 
 
 SMALL = ["C0", "S_softmax", "S_sigmoid", "S_selected", "S_capgate", "S_cap3shared", "S_f32",
-         "S_tied", "S_KeqN", "S_N1", "S_stream", "S_stream_cap"]
+         "S_tied", "S_KeqN", "S_N1", "S_stream", "S_stream_cap", "S_rankcap", "S_rankcap_stream"]
 _cache = {}
 
 
@@ -105,9 +105,10 @@ def test_permute_stage(name, copy_rows):
     z = O.router_logits(L.x_f(), inp.as_float(inp.w_router), inp.logit_bias)
     idx = O.topk_select(z, c.K)
     out = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity,
+                          capacity_group=c.capacity_group,
                           copy_rows=copy_rows)
     torch.cuda.synchronize()
-    kept = O.keep_routes(idx, c.N, L.capacity)
+    kept = L.keep(idx)
     perm = O.permutation(idx, kept, c.N)
     R = int(perm.offsets[-1])
     assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, c.N))
@@ -122,6 +123,38 @@ def test_permute_stage(name, copy_rows):
     xs = L.x[torch.from_numpy(perm.row_token).long().cuda()]
     assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
                        xs.view(torch.int16) if xs.dtype == torch.bfloat16 else xs.view(torch.int32))
+
+
+@pytest.mark.parametrize("N,K,group,budget", [(64, 4, 8, 1500), (64, 4, 8, 0), (64, 4, 64, 9000),
+                                               (64, 4, 1, 300), (256, 8, 32, 2000),
+                                               (16, 2, 4, 10 ** 6), (5, 3, 5, 7)])
+def test_rank_wide_capacity_permute(N, K, group, budget):
+    """Rank-wide capacity (Section 10.3, Eq. 23): kept counts, offsets and the restoration
+    map bit-exact against the oracle's admission (local-expert-major, then source rank,
+    prefix per split, four contiguous source shards), and the drops of every destination
+    equal [R_q^req - B]_+ (Eq. 28)."""
+    say(f"rank-wide capacity N={N} K={K} group={group} budget={budget}")
+    rng = np.random.default_rng(N + K + group)
+    T = 64 * 70 + 13
+    z = (rng.standard_normal((T, N)) + 2.0 * np.log(1.0 / np.arange(1, N + 1) ** 1.1)).astype(np.float32)
+    idx = O.topk_select(z, K)
+    x = torch.zeros(T, 64, dtype=torch.bfloat16, device="cuda")
+    out = moe.moe_permute(x, torch.from_numpy(idx).cuda(), N, budget, copy_rows=False,
+                          capacity_group=group)
+    torch.cuda.synchronize()
+    kept = O.keep_routes_rank_wide(idx, N, group, budget, n_sources=4)
+    perm = O.permutation(idx, kept, N)
+    R = int(perm.offsets[-1])
+    assert np.array_equal(host(out["C_keep"]), perm.C_keep)
+    assert np.array_equal(host(out["offsets"]), perm.offsets)
+    assert np.array_equal(host(out["dest_row"]), perm.dest_row)
+    assert np.array_equal(host(out["row_token"])[:R], perm.row_token)
+    Rq_req = O.rank_loads(host(out["C_req"]), group)
+    Rq_keep = O.rank_loads(host(out["C_keep"]), group)
+    assert [int(a - b) for a, b in zip(Rq_req, Rq_keep)] == \
+        [O.drops_rank_wide(host(out["C_req"])[q * group:(q + 1) * group], budget)
+         for q in range(N // group)]
+    say(f"  kept {R} of {K * T}; destination loads kept {Rq_keep.tolist()[:8]}")
 
 
 # ---------------------------------------------------------------------------------------
@@ -245,9 +278,10 @@ def test_expert_stage(name):
     inp = L.inp
     z = O.router_logits(L.x_f(), inp.as_float(inp.w_router), inp.logit_bias)
     idx = O.topk_select(z, c.K)
-    pm = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity, copy_rows=False)
-    perm = O.permutation(idx, O.keep_routes(idx, c.N, L.capacity), c.N)
-    rows = moe.max_rows(L.T, c.N, c.K, L.capacity)
+    pm = moe.moe_permute(L.x, torch.from_numpy(idx).cuda(), c.N, L.capacity, copy_rows=False,
+                         capacity_group=c.capacity_group)
+    perm = O.permutation(idx, L.keep(idx), c.N)
+    rows = moe.max_rows(L.T, c.N, c.K, L.capacity, c.capacity_group)
     wg, wu, wd = (moe.moe_pack_weights(w) for w in (L.w_gate, L.w_up, L.w_down))
     sm = moe.pack_shared(L.shared) if L.shared else None
     if sm is not None:
@@ -331,7 +365,7 @@ def check_forward(L: DeviceLayer, full=True, sample_tokens=None, keep_x_perm=Fal
         idx = O.topk_select(z_gpu, c.K)
         r = O.route_coefficients(z_gpu.astype(np.float64), idx, c.score, c.renorm, c.alpha)
         s_tok = None if inp.w_shared_gate is None else O.shared_gate(L.x_f(), inp.as_float(inp.w_shared_gate))
-        perm = O.permutation(idx, O.keep_routes(idx, c.N, L.capacity), c.N)
+        perm = O.permutation(idx, L.keep(idx), c.N)
     R = int(perm.offsets[-1])
     assert np.array_equal(host(o["topk_idx"]), idx)
     assert np.max(np.abs(host(o["topk_r"]) - r)) <= F32_MAX_ABS

@@ -31,12 +31,12 @@ def setup_module(module):
     moe = m
 
 
-def oracle_stats(o, N, score):
+def oracle_stats(o, N, score, group=0):
     z = host(o["logits"]).astype(np.float64)
     idx = host(o["topk_idx"])
     kept = host(o["dest_row"]) >= 0
     r = host(o["topk_r"]).astype(np.float64)
-    return O.balance_stats(O.normalized_scores(z, score), idx, kept, r, N)
+    return O.balance_stats(O.normalized_scores(z, score), idx, kept, r, N, group=group)
 
 
 def compare(P, st: dict, ref: O.BalanceStats, what: str):
@@ -53,7 +53,8 @@ def compare(P, st: dict, ref: O.BalanceStats, what: str):
 
 
 @pytest.mark.parametrize("name", ["C0", "S_softmax", "S_sigmoid", "S_selected", "S_capgate",
-                                  "S_cap3shared", "S_f32", "S_KeqN", "S_N1", "S_stream_cap"])
+                                  "S_cap3shared", "S_f32", "S_KeqN", "S_N1", "S_stream_cap",
+                                  "S_rankcap", "S_rankcap_stream"])
 def test_balance_stats_match_oracle(name):
     L = DeviceLayer(synth.get_config(name))
     c = L.cfg
@@ -63,11 +64,11 @@ def test_balance_stats_match_oracle(name):
     lay.forward()
     torch.cuda.synchronize()
     o = lay.out
-    ref = oracle_stats(o, c.N, c.score)
+    ref = oracle_stats(o, c.N, c.score, c.capacity_group)
     compare(o["balance_P"], moe.stats_dict(o["balance_stats"]), ref, f"{name} (forward)")
     # the standalone entry point on the same routing gives the same bits
     P, st = moe.moe_balance_stats(o["logits"], o["C_req"], o["C_keep"], o["dest_row"],
-                                  o["topk_r"], score=c.score)
+                                  o["topk_r"], score=c.score, expert_group=c.capacity_group)
     torch.cuda.synchronize()
     assert torch.equal(P, o["balance_P"])
     assert torch.equal(st.view(torch.int32), o["balance_stats"].view(torch.int32))
@@ -114,13 +115,14 @@ def test_balance_stats_on_given_logits_many_blocks():
     cap = int(np.median(C_req))
     kept = O.keep_routes(idx, N, cap)
     perm = O.permutation(idx, kept, N)
-    for score in (O.SOFTMAX, O.SIGMOID):
+    for score, group in ((O.SOFTMAX, 0), (O.SIGMOID, 32), (O.SOFTMAX, 256), (O.SIGMOID, 1)):
         r = O.route_coefficients(z.astype(np.float64), idx, score, True, 1.0).astype(np.float32)
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         P, st = moe.moe_balance_stats(dev(z), dev(C_req.astype(np.int32)),
                                       dev(perm.C_keep.astype(np.int32)),
-                                      dev(perm.dest_row.astype(np.int32)), dev(r), score=score)
+                                      dev(perm.dest_row.astype(np.int32)), dev(r), score=score,
+                                      expert_group=group)
         torch.cuda.synchronize()
         ref = O.balance_stats(O.normalized_scores(z.astype(np.float64), score), idx, kept,
-                              r.astype(np.float64), N)
-        compare(P, moe.stats_dict(st), ref, f"synthetic score={score}")
+                              r.astype(np.float64), N, group=group)
+        compare(P, moe.stats_dict(st), ref, f"synthetic score={score} group={group}")
