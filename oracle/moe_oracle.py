@@ -94,6 +94,35 @@ def topk_select(keys, K: int) -> np.ndarray:
     return order[:, :K].astype(np.int32)
 
 
+def selection_keys(z, score: int, expert_bias=None) -> np.ndarray:
+    """Keys of auxiliary-loss-free biased selection S_t = TopK_i(a_{t,i} + b_i) (p5
+    Eq. 35): a = z for the softmax rules, a = sigmoid(z) for sigmoid affinities. The
+    persistent bias b moves only the selection, never the weights. Without a bias the
+    keys are the logits themselves (sigmoid is monotone). The sum is taken in the
+    precision of the inputs (pass float32 logits and bias to decide in float32)."""
+    z = np.asarray(z)
+    if expert_bias is None:
+        return z
+    b = np.asarray(expert_bias, dtype=z.dtype)
+    a = 1.0 / (1.0 + np.exp(-z)) if score == SIGMOID else z
+    return a.astype(z.dtype) + b[None, :]
+
+
+def bias_update(expert_bias, C_fb, gamma: float) -> np.ndarray:
+    """One step of the hard-count controller (p5 Eq. 36-37):
+    b_i <- b_i + gamma sign(mean(C^fb) - C_i^fb) over a feedback window of requested
+    counts. The sign is taken exactly, as sign(sum_j C_j - N C_i); the bias is kept in
+    float32, the precision the selection keys use, and an expert exactly at the mean is
+    left untouched."""
+    C = np.asarray(C_fb, dtype=np.int64)
+    N = C.size
+    sgn = np.sign(C.sum() - N * C)
+    b = np.asarray(expert_bias, dtype=np.float32).copy()
+    moved = sgn != 0
+    b[moved] = b[moved] + np.float32(gamma) * sgn[moved].astype(np.float32)
+    return b
+
+
 def route_coefficients(z, idx, score: int, renorm: bool, alpha: float) -> np.ndarray:
     """r_{t,k} for the selected experts.
 
@@ -431,6 +460,7 @@ class LayerSpec:
     s: float = 1.0                    # fixed shared gain when there is no learned gate
     capacity: int = -1                # routes kept per expert (or per destination); < 0 = unlimited
     capacity_group: int = 0           # > 0: destinations of this many experts share `capacity`
+    expert_bias: Optional[np.ndarray] = None   # [N] selection-only bias b (p5 Eq. 35)
 
 
 @dataclass
@@ -460,9 +490,9 @@ def forward(spec: LayerSpec, x, w_router, expert_weights: Callable[[int], tuple]
     x = _f64(x)
     T = x.shape[0]
     z = router_logits(x, w_router, logit_bias)
-    keys = z if logits_override is None else np.asarray(logits_override)
-    idx = topk_select(keys, spec.K)
-    r = route_coefficients(keys, idx, spec.score, spec.renorm, spec.alpha)
+    zz = z if logits_override is None else np.asarray(logits_override)
+    idx = topk_select(selection_keys(zz, spec.score, spec.expert_bias), spec.K)
+    r = route_coefficients(zz, idx, spec.score, spec.renorm, spec.alpha)
     s_tok = shared_gate(x, w_shared_gate) if w_shared_gate is not None else None
     C_req = requested_counts(idx, spec.N)
     if spec.capacity_group > 0:

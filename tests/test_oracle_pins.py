@@ -721,3 +721,84 @@ def test_rank_level_imbalance():
     assert math.isnan(O.balance_stats(p, idx, kept, r, N).imax_rank_req)
     with pytest.raises(ValueError):
         O.destination_of(6, 4)
+
+
+# ---------------------------------------------------------------------------------------
+# f3: auxiliary-loss-free biased selection and the hard-count controller
+# ---------------------------------------------------------------------------------------
+def test_biased_selection_eq35_by_hand():
+    """p5 Eq. 35: the bias moves the selection, the weights come from the unbiased
+    affinities renormalized over the selected set. Two tokens, three experts, K = 2:
+    z = (2, 1, 0) selects {0, 1}; b = (0, 0, 1.5) makes the keys (2, 1, 1.5) and selects
+    {0, 2}, weighted e^2 / (e^2 + e^0) and e^0 / (e^2 + e^0) (softmax, alpha = 1)."""
+    z = np.array([[2.0, 1.0, 0.0], [0.0, 0.0, 0.0]])
+    b = np.array([0.0, 0.0, 1.5])
+    assert O.topk_select(O.selection_keys(z, O.SOFTMAX), 2).tolist() == [[0, 1], [0, 1]]
+    idx = O.topk_select(O.selection_keys(z, O.SOFTMAX, b), 2)
+    assert idx.tolist() == [[0, 2], [2, 0]]
+    r = O.route_coefficients(z, idx, O.SOFTMAX, True, 1.0)
+    e2 = math.exp(2.0)
+    assert np.allclose(r[0], [e2 / (e2 + 1), 1 / (e2 + 1)], rtol=0, atol=1e-15)
+    assert np.allclose(r[1], [0.5, 0.5], rtol=0, atol=1e-15)   # unbiased z ties: equal weights
+    # sigmoid affinities: a = omega = sigma(z); keys sigma(z) + b
+    zs = np.array([[0.0, 3.0, -3.0]])
+    sig = 1 / (1 + np.exp(-zs[0]))
+    keys = O.selection_keys(zs, O.SIGMOID, np.array([0.6, 0.0, 0.0]))
+    assert np.allclose(keys[0], sig + [0.6, 0, 0], rtol=0, atol=1e-15)
+    idx = O.topk_select(keys, 2)
+    assert idx.tolist() == [[0, 1]]                               # 1.1 > 0.953 > 0.047
+    r = O.route_coefficients(zs, idx, O.SIGMOID, True, 2.5)
+    assert np.allclose(r[0], 2.5 * sig[[0, 1]] / sig[[0, 1]].sum(), rtol=0, atol=1e-15)
+
+
+def test_zero_bias_is_plain_selection_and_large_bias_forces_an_expert():
+    """b = 0 reduces Eq. 35 to the unbiased top-K; a bias above the spread of the keys
+    puts its expert in every token's set without changing the unbiased weights."""
+    rng = np.random.default_rng(8)
+    T, N, K = 200, 12, 3
+    z = rng.standard_normal((T, N)).astype(np.float32)
+    assert np.array_equal(O.topk_select(O.selection_keys(z, O.SOFTMAX, np.zeros(N)), K),
+                          O.topk_select(z, K))
+    for score in (O.SOFTMAX, O.SIGMOID, O.SOFTMAX_SELECTED):
+        b = np.zeros(N, dtype=np.float32)
+        b[7] = 100.0
+        idx = O.topk_select(O.selection_keys(z, score, b), K)
+        assert (idx[:, 0] == 7).all()
+        r = O.route_coefficients(z.astype(np.float64), idx, score, True, 1.0)
+        assert np.allclose(r.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_bias_update_eq36_eq37():
+    """p5 Eq. 36-37 by hand: C = (6, 2, 4), mean 4: the overloaded expert falls by gamma,
+    the underloaded rises, the one at the mean stays; a half-integer mean C = (1, 2)
+    gives signs (+1, -1); requested counts, not kept ones, drive the update."""
+    b = O.bias_update(np.zeros(3), [6, 2, 4], 0.25)
+    assert b.tolist() == [-0.25, 0.25, 0.0] and b.dtype == np.float32
+    assert O.bias_update(np.array([1.0, 1.0]), [1, 2], 0.5).tolist() == [1.5, 0.5]
+    assert O.bias_update(np.array([-0.0, 3.0]), [5, 5], 1.0).tolist() == [-0.0, 3.0]
+    # float32 accumulation: 0.1 added ten times in float32
+    b = np.zeros(2, dtype=np.float32)
+    for _ in range(10):
+        b = O.bias_update(b, [0, 4], 0.1)
+    acc = np.float32(0)
+    for _ in range(10):
+        acc = np.float32(acc + np.float32(0.1))
+    assert b[0] == acc and b[1] == -acc
+
+
+def test_bias_controller_moves_load_toward_balance():
+    """p5 Section 10.6: underloaded experts gain selection offset, overloaded ones lose
+    it; on a fixed skewed batch the requested max/mean imbalance falls."""
+    rng = np.random.default_rng(4)
+    T, N, K = 512, 16, 2
+    z = (rng.standard_normal((T, N)) + 1.5 * np.log(1.0 / np.arange(1, N + 1))).astype(np.float32)
+    b = np.zeros(N, dtype=np.float32)
+    C0 = O.requested_counts(O.topk_select(z, K), N)
+    for _ in range(60):
+        C = O.requested_counts(O.topk_select(O.selection_keys(z, O.SOFTMAX, b), K), N)
+        b_new = O.bias_update(b, C, 0.05)
+        over, under = C > C.mean(), C < C.mean()
+        assert (b_new[over] < b[over]).all() and (b_new[under] > b[under]).all()
+        b = b_new
+    C = O.requested_counts(O.topk_select(O.selection_keys(z, O.SOFTMAX, b), K), N)
+    assert O.imbalance_max(C) < 0.5 * O.imbalance_max(C0)
