@@ -100,6 +100,11 @@ int moe_max_rows(int T, int N, int K, int capacity, int capacity_group);
  *   x                  [T][d_model]
  *   w_router           [N][d_model]
  *   logit_bias         [N] float32 added to every logit, or NULL
+ *   expert_bias        [N] float32 persistent selection bias b of auxiliary-loss-free
+ *                      balancing (Section 10 Eq. 35), or NULL: experts are selected by
+ *                      TopK(a + b) with a = z (softmax rules) or sigmoid(z) (sigmoid
+ *                      affinities), summed in float32; the coefficients still come from
+ *                      the unbiased logits of the selected experts
  *   w_shared_gate      [d_model] (dtype dt) learned shared-gate vector w_s, or NULL;
  *                      when given, s_tok[t] = sigmoid(x_t . w_s) (Table 52, Qwen rows)
  *   logits             [T][N] float32: logits_mode 0 -> output (z + b), may be NULL;
@@ -114,9 +119,25 @@ int moe_max_rows(int T, int N, int K, int capacity, int capacity_group);
 size_t moe_route_workspace_size(int T, int N, int K);
 int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
               const void* x, const void* w_router, const float* logit_bias,
-              const void* w_shared_gate, float* logits, int logits_mode, int32_t* topk_idx,
-              float* topk_r, float* s_tok, int32_t* C_req, void* workspace,
-              size_t workspace_bytes, hipStream_t stream);
+              const float* expert_bias, const void* w_shared_gate, float* logits,
+              int logits_mode, int32_t* topk_idx, float* topk_r, float* s_tok, int32_t* C_req,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_bias_update: one step of the hard-count controller of auxiliary-loss-free
+ * balancing (Section 10 Eq. 36-37), outside any gradient:
+ *   b_i <- b_i + gamma sign(mean_j C_j - C_i)
+ * over the requested counts C accumulated during one feedback window (for example by
+ * moe_forward_args.count_accum across the microbatches of a batch). The sign is decided
+ * exactly in 64-bit integers; an expert exactly at the mean keeps its bias.
+ *
+ *   count_accum        [N] int32 device, in; set to zero afterwards when reset = 1
+ *   expert_bias        [N] float32 device, updated in place
+ * Returns MOE_ERR_INVALID_ARG for N <= 0, a NULL pointer, reset not 0/1 or a non-finite
+ * gamma, MOE_ERR_UNSUPPORTED for N > 256.
+ * ------------------------------------------------------------------------------- */
+int moe_bias_update(int N, float gamma, int32_t* count_accum, float* expert_bias, int reset,
+                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_permute: requested counts, capacity admission, offsets, restoration map and the
@@ -331,6 +352,7 @@ typedef struct moe_forward_args {
   const void* x;         /* [T][d_model] */
   const void* w_router;  /* [N][d_model] */
   const float* logit_bias;    /* [N] or NULL */
+  const float* expert_bias;   /* [N] selection-only bias (moe_route), or NULL */
   const void* w_shared_gate;  /* [d_model] or NULL */
   const void* w_gate;    /* [N][d_r][d_model] */
   const void* w_up;      /* [N][d_r][d_model] */
@@ -361,6 +383,9 @@ typedef struct moe_forward_args {
    * MOE_ERR_INVALID_ARG): */
   float* balance_P;      /* [N] */
   float* balance_stats;  /* [MOE_STAT_COUNT] */
+  /* Feedback-window counts for moe_bias_update: C_req of this batch is added to it when
+   * non-NULL ([N] int32, zeroed by the caller or by moe_bias_update's reset). */
+  int32_t* count_accum;
 } moe_forward_args;
 
 size_t moe_forward_workspace_size(const moe_forward_args* args);

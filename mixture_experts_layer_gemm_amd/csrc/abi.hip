@@ -166,9 +166,9 @@ size_t moe_route_workspace_size(int T, int N, int K) {
 
 int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
               const void* x, const void* w_router, const float* logit_bias,
-              const void* w_shared_gate, float* logits, int logits_mode, int32_t* topk_idx,
-              float* topk_r, float* s_tok, int32_t* C_req, void* workspace,
-              size_t workspace_bytes, hipStream_t stream) {
+              const float* expert_bias, const void* w_shared_gate, float* logits,
+              int logits_mode, int32_t* topk_idx, float* topk_r, float* s_tok, int32_t* C_req,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE_TRY(check_router_dims(T, d_model, N, K));
   MOE_TRY(check_dtype(dt));
   if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
@@ -185,11 +185,11 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
     carve_count(workspace, T, N, K, true, &w);
   }
   MOE_HIP(launch_route(T, d_model, N, K, score, renorm, alpha, dt, x, w_router, logit_bias,
-                       logits_mode == 0 ? w_shared_gate : nullptr, logits, logits_mode,
-                       topk_idx, topk_r, s_tok, stream));
+                       expert_bias, logits_mode == 0 ? w_shared_gate : nullptr, logits,
+                       logits_mode, topk_idx, topk_r, s_tok, stream));
   if (C_req) {
     MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-    MOE_HIP(launch_scan(T, N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, stream));
+    MOE_HIP(launch_scan(T, N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, nullptr, stream));
   }
   return MOE_OK;
 }
@@ -214,7 +214,8 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_gro
   CountWs w{};
   carve_count(workspace, T, N, K, false, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, stream));
+  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
+                      stream));
   MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
                          dest_row, row_token, x_perm, stream));
   return MOE_OK;
@@ -414,6 +415,16 @@ int moe_balance_stats(int T, int N, int K, int score, int expert_group, const fl
   return MOE_OK;
 }
 
+int moe_bias_update(int N, float gamma, int32_t* count_accum, float* expert_bias, int reset,
+                    hipStream_t stream) {
+  if (N <= 0 || !count_accum || !expert_bias || (reset != 0 && reset != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (N > moe::kMaxN) return MOE_ERR_UNSUPPORTED;
+  if (!std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_bias_update(N, gamma, count_accum, expert_bias, reset, stream));
+  return MOE_OK;
+}
+
 size_t moe_forward_workspace_size(const moe_forward_args* a) {
   if (!a || a->T <= 0 || a->N <= 0 || a->K <= 0 || a->d_model <= 0) return 0;
   return carve_forward(a, nullptr, nullptr);
@@ -442,11 +453,11 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   const int T = a->T, d = a->d_model, N = a->N, K = a->K;
   const int rows = moe_max_rows(T, N, K, a->capacity, a->capacity_group);
   MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
-                       a->logit_bias, a->w_shared_gate, w.logits, 0, w.topk_idx, w.topk_r,
-                       w.s_tok, stream));
+                       a->logit_bias, a->expert_bias, a->w_shared_gate, w.logits, 0, w.topk_idx,
+                       w.topk_r, w.s_tok, stream));
   MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, a->capacity, a->capacity_group, w.hist, w.C_req, w.C_keep,
-                      w.offsets, stream));
+                      w.offsets, a->count_accum, stream));
   MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
                          w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
   MOE_HIP(expert_passes(N, d, a->d_r, a->d_s, a->dt, a->weights_packed == 1, a->x, T,

@@ -55,18 +55,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // ---------------------------------------------------------------------------------
 // launchers (enqueue only; return hipError_t of the launch)
 // ---------------------------------------------------------------------------------
+// expert_bias: selection-only bias b of auxiliary-loss-free balancing, or nullptr
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
-                        const void* w_shared_gate, float* logits, int logits_mode,
+                        const float* expert_bias, const void* w_shared_gate, float* logits,
+                        int logits_mode,
                         int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream);
 
 hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
                         int32_t* loc_rank, hipStream_t stream);
 
 // capacity < 0: keep every route; group == 0: per-expert limit; group > 0: one budget
-// `capacity` shared by each run of `group` consecutive experts
+// `capacity` shared by each run of `group` consecutive experts. count_accum (or nullptr)
+// gets C_req added (feedback-window counts of the bias controller).
 hipError_t launch_scan(int T, int N, int capacity, int group, int32_t* hist, int32_t* C_req,
-                       int32_t* C_keep, int32_t* offsets, hipStream_t stream);
+                       int32_t* C_keep, int32_t* offsets, int32_t* count_accum,
+                       hipStream_t stream);
+
+// b_i += gamma sign(sum_j C_j - N C_i); C zeroed when reset != 0
+hipError_t launch_bias_update(int N, float gamma, int32_t* count_accum, float* expert_bias,
+                              int reset, hipStream_t stream);
 
 // x_perm == nullptr: restoration map only (no row copy)
 hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* x,

@@ -71,7 +71,7 @@ constexpr int SCAN_THREADS = 1024;
 __global__ void __launch_bounds__(SCAN_THREADS)
 scan_kernel(int nchunks, int N, int NP, int capacity, int group, int32_t* __restrict__ hist,
             int32_t* __restrict__ C_req, int32_t* __restrict__ C_keep,
-            int32_t* __restrict__ offsets) {
+            int32_t* __restrict__ offsets, int32_t* __restrict__ count_accum) {
   __shared__ int32_t part[SCAN_THREADS];
   __shared__ int32_t req[kMaxN];
   __shared__ int32_t keep[kMaxN];
@@ -120,6 +120,7 @@ scan_kernel(int nchunks, int N, int NP, int capacity, int group, int32_t* __rest
     if (p == P - 1) {
       C_req[e] = run;
       req[e] = run;
+      if (count_accum != nullptr) count_accum[e] += run;
     }
   }
   __syncthreads();
@@ -228,12 +229,13 @@ hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* h
 }
 
 hipError_t launch_scan(int T, int N, int capacity, int group, int32_t* hist, int32_t* C_req,
-                       int32_t* C_keep, int32_t* offsets, hipStream_t stream) {
+                       int32_t* C_keep, int32_t* offsets, int32_t* count_accum,
+                       hipStream_t stream) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   int NP = 1;
   while (NP < N) NP <<= 1;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, nchunks, N, NP,
-                     capacity, group, hist, C_req, C_keep, offsets);
+                     capacity, group, hist, C_req, C_keep, offsets, count_accum);
   return hipGetLastError();
 }
 

@@ -13,6 +13,11 @@
 // fixed order. Phase 2 gives each wave BT / waves tokens: top-K by K rounds of a
 // wave-wide max over packed (ordered float key, inverted expert index) 64-bit values,
 // which yields the lowest index on ties, then the coefficients in the lanes k < K.
+//
+// Auxiliary-loss-free balancing ("Section 10: Routing, Capacity, and Load Balancing",
+// Eq. 35): with a persistent expert bias b the keys become z + b (softmax rules) or
+// sigmoid(z) + b (sigmoid affinities), summed in fp32, while the coefficients are still
+// computed from the unbiased logits of the selected experts.
 #include "common.h"
 
 using namespace moe;
@@ -147,7 +152,8 @@ template <int BT, int NBT, int WAVES, int U>
 __global__ void __launch_bounds__(WAVES * 64)
 route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
              const void* __restrict__ x, const void* __restrict__ w_router,
-             const float* __restrict__ logit_bias, const void* __restrict__ w_gate_vec,
+             const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
+             const void* __restrict__ w_gate_vec,
              float* __restrict__ logits, int logits_mode, int32_t* __restrict__ topk_idx,
              float* __restrict__ topk_r, float* __restrict__ s_tok) {
   constexpr int THREADS = WAVES * 64;
@@ -200,6 +206,13 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   // ---- phase 2: top-K and coefficients, one wave per token --------------------------
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const bool biased = sel_bias != nullptr;
+  float bias_r[kMaxN / kWave];
+#pragma unroll
+  for (int j = 0; j < kMaxN / kWave; ++j) {
+    const int e = lane + j * kWave;
+    bias_r[j] = (biased && e < N) ? sel_bias[e] : 0.f;
+  }
   for (int t = w; t < BT; t += WAVES) {
     const int tok = t0 + t;
     if (tok >= T) break;
@@ -208,7 +221,12 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
 #pragma unroll
     for (int j = 0; j < kMaxN / kWave; ++j) {
       const int e = lane + j * kWave;
-      cand[j] = (e < N) ? ((static_cast<uint64_t>(ord_key(zr[e])) << 32) |
+      float key = 0.f;
+      if (e < N) {
+        key = zr[e];
+        if (biased) key = (score == 1 ? sigmoid_f(key) : key) + bias_r[j];
+      }
+      cand[j] = (e < N) ? ((static_cast<uint64_t>(ord_key(key)) << 32) |
                            static_cast<uint64_t>(~static_cast<uint32_t>(e)))
                         : 0ull;
     }
@@ -221,7 +239,7 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
       m = wave_max_u64(m);
       const int e = static_cast<int>(~static_cast<uint32_t>(m));
       if (lane == k) {
-        selz = unord_key(static_cast<uint32_t>(m >> 32));
+        selz = biased ? zr[e] : unord_key(static_cast<uint32_t>(m >> 32));
         sele = e;
       }
 #pragma unroll
@@ -234,7 +252,21 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
       const float a = act ? sigmoid_f(selz) : 0.f;
       r = renorm ? alpha * a / wave_sum(a) : alpha * a;
     } else {
-      const float m = __shfl(selz, 0, kWave);  // top-1 logit = max over all N
+      // max over all N logits: the top-1 key unless a bias reordered the selection
+      float m;
+      if (biased) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMaxN / kWave; ++j) {
+          const int ee = lane + j * kWave;
+          if (ee < N) mx = fmaxf(mx, zr[ee]);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+        m = mx;
+      } else {
+        m = __shfl(selz, 0, kWave);
+      }
       const float e = act ? expf(selz - m) : 0.f;
       if (score == 0 && !renorm) {
         float zsum = 0.f;
@@ -259,11 +291,12 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
 template <int BT, int NBT, int WAVES, int U>
 hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
                       const void* x, const void* w_router, const float* logit_bias,
-                      const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
+                      const float* sel_bias, const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
                       float* topk_r, float* s_tok, hipStream_t stream) {
   const int grid = (T + BT - 1) / BT;
   hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U>), dim3(grid), dim3(WAVES * 64), 0, stream,
-                     T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, w_gate_vec,
+                     T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, sel_bias,
+                     w_gate_vec,
                      logits, logits_mode, topk_idx, topk_r, s_tok);
   return hipGetLastError();
 }
@@ -272,7 +305,7 @@ hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float a
 
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
-                        const void* w_shared_gate, float* logits, int logits_mode,
+                        const float* expert_bias, const void* w_shared_gate, float* logits, int logits_mode,
                         int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream) {
   const int ncol = N + ((w_shared_gate != nullptr && logits_mode == 0) ? 1 : 0);
   const int NB = (ncol + 15) / 16;
@@ -281,8 +314,9 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
 #define MOE_ROUTE_CASE(BT_, NBT_, W_, U_)                                                    \
   if (NB <= NBT_)                                                                            \
     return launch_cfg<BT_, NBT_, W_, U_>(T, d_model, N, K, score, renorm, alpha, dt, x,      \
-                                         w_router, logit_bias, w_shared_gate, logits,        \
-                                         logits_mode, topk_idx, topk_r, s_tok, stream);
+                                         w_router, logit_bias, expert_bias, w_shared_gate,   \
+                                         logits, logits_mode, topk_idx, topk_r, s_tok,       \
+                                         stream);
   MOE_ROUTE_CASE(16, 1, 8, 8)
   MOE_ROUTE_CASE(16, 2, 8, 8)
   MOE_ROUTE_CASE(16, 4, 8, 4)

@@ -35,11 +35,12 @@ class ForwardArgs(ctypes.Structure):
         ("alpha", c_float), ("s", c_float), ("capacity", c_int), ("capacity_group", c_int),
         ("dt", c_int),
         ("weights_packed", c_int)] + [
-        (n, c_void_p) for n in ("x", "w_router", "logit_bias", "w_shared_gate", "w_gate", "w_up",
+        (n, c_void_p) for n in ("x", "w_router", "logit_bias", "expert_bias", "w_shared_gate",
+                                "w_gate", "w_up",
                                 "w_down", "ws_gate", "ws_up", "ws_down", "y", "logits", "topk_idx",
                                 "topk_r", "s_tok", "C_req", "C_keep", "offsets", "dest_row",
                                 "row_token", "x_perm", "h_perm", "f_perm", "g", "balance_P",
-                                "balance_stats")]
+                                "balance_stats", "count_accum")]
 
 # order of moe_balance_stats' output vector (enum moe_stat)
 STAT_NAMES = ["lbl", "imax_req", "imax_keep", "ih_req", "ih_keep", "cv_req", "cv_keep",
@@ -59,7 +60,8 @@ def _load() -> ctypes.CDLL:
         "moe_rank_capacity_from_factor": (I, [c_double, I, I]),
         "moe_max_rows": (I, [I, I, I, I, I]),
         "moe_route_workspace_size": (S, [I, I, I]),
-        "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, I, P, P, P, P, P, S, P]),
+        "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, I, P, P, P, P, P, S, P]),
+        "moe_bias_update": (I, [I, F, P, P, I, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
         "moe_grouped_swiglu": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P]),
@@ -140,8 +142,10 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = True,
               alpha: float = 1.0, logit_bias=None, w_shared_gate=None, logits=None,
-              logits_mode: int = 0, want_logits: bool = False, want_counts: bool = True):
-    """Router stage. Returns dict(topk_idx, topk_r, s_tok, C_req, logits)."""
+              logits_mode: int = 0, want_logits: bool = False, want_counts: bool = True,
+              expert_bias=None):
+    """Router stage. Returns dict(topk_idx, topk_r, s_tok, C_req, logits). expert_bias is
+    the selection-only bias of auxiliary-loss-free balancing."""
     if logits_mode == 1:
         T, N = logits.shape
         dev, d, dt = logits.device, 64, MOE_F32
@@ -161,12 +165,20 @@ def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = Tr
     st = lib.moe_route(T, d, N, K, score, int(renorm), float(alpha), dt,
                        None if logits_mode == 1 else _ptr(x),
                        None if logits_mode == 1 else _ptr(w_router),
-                       None if logits_mode == 1 else _ptr(logit_bias),
+                       None if logits_mode == 1 else _ptr(logit_bias), _ptr(expert_bias),
                        None if logits_mode == 1 else _ptr(w_shared_gate),
                        _ptr(logits), logits_mode, _ptr(out["topk_idx"]), _ptr(out["topk_r"]),
                        _ptr(out["s_tok"]), _ptr(out["C_req"]), _ptr(ws), ws.numel(), _stream())
     _check("moe_route", st)
     return out
+
+
+def moe_bias_update(count_accum, expert_bias, gamma: float, reset: bool = True):
+    """b_i += gamma sign(mean(C) - C_i) in place over the accumulated requested counts;
+    the accumulator is zeroed when reset."""
+    st = lib.moe_bias_update(expert_bias.numel(), float(gamma), _ptr(count_accum),
+                             _ptr(expert_bias), int(reset), _stream())
+    _check("moe_bias_update", st)
 
 
 def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True,
@@ -315,7 +327,8 @@ class MoELayer:
     def __init__(self, x, w_router, w_gate, w_up, w_down, K: int, score: int = SCORE_SOFTMAX,
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
                  capacity_group: int = 0, logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
-                 pack_weights=None, keep_x_perm=False, balance_stats=False):
+                 pack_weights=None, keep_x_perm=False, balance_stats=False, expert_bias=None,
+                 count_accum=None):
         self.x = x
         T, d = x.shape
         N, d_r, _ = w_gate.shape
@@ -329,7 +342,8 @@ class MoELayer:
             if shared_mlp:
                 shared_mlp = tuple(moe_pack_weights(w[None])[0] for w in shared_mlp)
         self.tensors = dict(w_router=w_router, w_gate=w_gate, w_up=w_up, w_down=w_down,
-                            logit_bias=logit_bias, w_shared_gate=w_shared_gate)  # kept alive
+                            logit_bias=logit_bias, w_shared_gate=w_shared_gate,
+                            expert_bias=expert_bias, count_accum=count_accum)  # kept alive
         self.shared_mlp = shared_mlp      # (gate, up, down) of the one shared MLP, or None
         d_s = shared_mlp[0].shape[0] if shared_mlp else 0
         self.y = torch.empty(T, d, dtype=x.dtype, device=dev)
@@ -343,6 +357,7 @@ class MoELayer:
         a.x, a.w_router, a.w_gate, a.w_up, a.w_down = (_ptr(x), _ptr(w_router), _ptr(w_gate),
                                                        _ptr(w_up), _ptr(w_down))
         a.logit_bias, a.w_shared_gate = _ptr(logit_bias), _ptr(w_shared_gate)
+        a.expert_bias, a.count_accum = _ptr(expert_bias), _ptr(count_accum)
         if shared_mlp:
             a.ws_gate, a.ws_up, a.ws_down = (_ptr(p) for p in shared_mlp)
         a.y = _ptr(self.y)

@@ -480,18 +480,24 @@ class Result:
 
 def forward(spec: LayerSpec, x, w_router, expert_weights: Callable[[int], tuple],
             shared_experts: Sequence = (), logit_bias=None, w_shared_gate=None,
-            logits_override=None) -> Result:
+            logits_override=None, selection_override=None) -> Result:
     """The whole layer forward, stage by stage (p5 Section 10 opening paragraph:
     router -> capacity -> dispatch -> grouped expert compute -> combine; p1 Eq. 80).
 
     `expert_weights(i)` returns (w_gate, w_up, w_down) of routed expert i.
     `logits_override` (e.g. float32 logits) replaces the computed logits for selection
-    and coefficients, so that near-ties are decided on identical values."""
+    and coefficients, so that near-ties are decided on identical values.
+    `selection_override` ([T, K] expert indices) replaces the top-K selection, for the
+    cases where several selections are correct within rounding (the caller checks that
+    the one it passes is among them)."""
     x = _f64(x)
     T = x.shape[0]
     z = router_logits(x, w_router, logit_bias)
     zz = z if logits_override is None else np.asarray(logits_override)
-    idx = topk_select(selection_keys(zz, spec.score, spec.expert_bias), spec.K)
+    if selection_override is None:
+        idx = topk_select(selection_keys(zz, spec.score, spec.expert_bias), spec.K)
+    else:
+        idx = np.asarray(selection_override).astype(np.int32)
     r = route_coefficients(zz, idx, spec.score, spec.renorm, spec.alpha)
     s_tok = shared_gate(x, w_shared_gate) if w_shared_gate is not None else None
     C_req = requested_counts(idx, spec.N)

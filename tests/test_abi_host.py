@@ -9,7 +9,7 @@ from mixture_experts_layer_gemm_amd import moe
 from mixture_experts_layer_gemm_amd import synth
 import oracle.moe_oracle as O
 
-EXPECTED = ["moe_balance_stats", "moe_balance_stats_workspace_size",
+EXPECTED = ["moe_balance_stats", "moe_balance_stats_workspace_size", "moe_bias_update",
             "moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
             "moe_forward_workspace_size",
             "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_pack_weights", "moe_permute",
@@ -77,7 +77,7 @@ def _route(**kw):
              gate=None, logits=None, mode=0, idx=1, r=1, s_tok=None, creq=None, ws=None, wsb=0)
     a.update(kw)
     return moe.lib.moe_route(a["T"], a["d"], a["N"], a["K"], a["score"], a["renorm"], a["alpha"],
-                             a["dt"], a["x"], a["w"], a["bias"], a["gate"], a["logits"], a["mode"],
+                             a["dt"], a["x"], a["w"], a["bias"], None, a["gate"], a["logits"], a["mode"],
                              a["idx"], a["r"], a["s_tok"], a["creq"], a["ws"], a["wsb"], None)
 
 
@@ -119,6 +119,11 @@ def test_permute_grouped_combine_forward_reject_bad_arguments():
     assert L.moe_grouped_gemm(1, 64, 128, 1, 1, 1, 1, 0, 1, None, 8, 1, 1, 1, None) == \
         moe.MOE_ERR_INVALID_ARG                               # row index needs a_rows
     assert L.moe_pack_weights(2, 64, 128, 0, 1, 2, None) == moe.MOE_ERR_UNSUPPORTED   # fp32
+    assert L.moe_bias_update(0, 0.1, 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(8, 0.1, None, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(8, 0.1, 1, 1, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(8, float("nan"), 1, 1, 1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(300, 0.1, 1, 1, 1, None) == moe.MOE_ERR_UNSUPPORTED
     bs = [64, 8, 2, 0, 0, 1, 1, 1, 1, 1, 1, 1]
     assert L.moe_balance_stats(*bs, None, 0, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_balance_stats(64, 8, 9, *bs[3:], 1, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG  # K > N

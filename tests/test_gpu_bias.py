@@ -1,0 +1,135 @@
+"""GPU parity of auxiliary-loss-free balancing (Section 10.6 of the routing page:
+Eq. 35 biased selection, Eq. 36-37 hard-count controller) against the oracle.
+
+Bars: selected experts bit-exact where both sides decide on identical float32 keys
+(softmax rules: z + b); for sigmoid affinities the keys sigmoid(z) + b pass through each
+side's own exponential, so a token may differ only where its K-th and (K+1)-th keys lie
+within float32 rounding, and the GPU's choice must then be a valid top-K of the exact
+keys. Coefficients within 1e-4 absolute (fp32), bias trajectories bit-exact (sign decided
+on integers, one float32 add per step), counts exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_layer_gemm_amd import synth
+from tests.gpu_common import DeviceLayer, assert_close, host, say, F32_MAX_ABS
+
+pytestmark = pytest.mark.gpu
+
+moe = None
+NEAR_TIE = 1e-6
+
+
+def setup_module(module):
+    global moe
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_gemm_amd import moe as m
+    moe = m
+
+
+def check_selection(idx_gpu, z32, b32, score, K):
+    """Exact agreement with the oracle's float32 decision, or (sigmoid keys only) a
+    near-tie where the GPU's set is still a valid top-K of the exact keys."""
+    ref = O.topk_select(O.selection_keys(z32, score, b32), K)
+    if score != O.SIGMOID:
+        assert np.array_equal(idx_gpu, ref)
+        return 0
+    bad = np.flatnonzero(np.any(idx_gpu != ref, axis=1))
+    k64 = O.selection_keys(z32.astype(np.float64), score, b32.astype(np.float64))
+    for t in bad:
+        sel = np.zeros(k64.shape[1], bool)
+        sel[idx_gpu[t]] = True
+        assert len(set(idx_gpu[t].tolist())) == K
+        assert k64[t, sel].min() >= k64[t, ~sel].max() - NEAR_TIE if (~sel).any() else True
+        assert np.all(np.diff(k64[t, idx_gpu[t]]) <= NEAR_TIE)       # slots by descending key
+    return len(bad)
+
+
+@pytest.mark.parametrize("N,K", [(8, 2), (64, 4), (256, 8), (16, 16), (5, 3)])
+@pytest.mark.parametrize("score,renorm", [(0, 1), (0, 0), (1, 1), (2, 1)])
+def test_biased_topk_on_identical_logits(N, K, score, renorm):
+    say(f"biased topk N={N} K={K} score={score} renorm={renorm}")
+    rng = np.random.default_rng(N * 31 + K)
+    T = 777
+    z = (rng.integers(-6, 7, size=(T, N)) * 0.25).astype(np.float32)   # exact ties in z
+    z[::5] = rng.standard_normal((len(z[::5]), N)).astype(np.float32)
+    b = (rng.integers(-4, 5, size=N) * 0.125).astype(np.float32)        # ties in z + b too
+    out = moe.moe_route(None, None, K, score=score, renorm=bool(renorm), alpha=1.5,
+                        logits=torch.from_numpy(z).cuda(), logits_mode=1,
+                        expert_bias=torch.from_numpy(b).cuda(), want_counts=True)
+    torch.cuda.synchronize()
+    idx = host(out["topk_idx"])
+    n = check_selection(idx, z, b, score, K)
+    assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, N))
+    r = O.route_coefficients(z.astype(np.float64), idx, score, bool(renorm), 1.5)
+    assert np.max(np.abs(host(out["topk_r"]) - r)) <= F32_MAX_ABS
+    say(f"  near-tie tokens: {n}")
+
+
+@pytest.mark.parametrize("name", ["S_softmax", "S_sigmoid", "S_selected", "S_capgate",
+                                  "S_stream_cap", "S_rankcap"])
+def test_forward_with_expert_bias(name):
+    """Whole layer with a selection bias: routing against the oracle, then every output
+    on that routing (the bias never enters the coefficients)."""
+    L = DeviceLayer(synth.get_config(name))
+    c = L.cfg
+    rng = np.random.default_rng(c.cfg_id)
+    b = (rng.standard_normal(c.N) * (0.05 if c.score == O.SIGMOID else 0.5)).astype(np.float32)
+    say(f"forward with expert bias {name}")
+    lay = moe.MoELayer(L.x, L.w_router, L.w_gate, L.w_up, L.w_down, c.K, keep_intermediates=True,
+                       expert_bias=torch.from_numpy(b).cuda(), **L.layer_kwargs())
+    y = lay.forward()
+    torch.cuda.synchronize()
+    o = lay.out
+    z = host(o["logits"])
+    idx = host(o["topk_idx"])
+    check_selection(idx, z, b, c.score, c.K)
+    spec = L.spec()
+    spec.expert_bias = b
+    inp = L.inp
+    res = O.forward(spec, L.x_f(), inp.as_float(inp.w_router), inp.expert_f32, inp.shared_f32(),
+                    logit_bias=inp.logit_bias,
+                    w_shared_gate=None if inp.w_shared_gate is None else inp.as_float(inp.w_shared_gate),
+                    logits_override=z, selection_override=idx)
+    assert np.max(np.abs(host(o["topk_r"]) - res.r)) <= F32_MAX_ABS
+    assert np.array_equal(host(o["C_keep"]), res.perm.C_keep)
+    assert np.array_equal(host(o["dest_row"]), res.perm.dest_row)
+    err = assert_close(host(y), res.y, c.dtype, "y")
+    unbiased = O.topk_select(z, c.K)
+    say(f"  tokens whose selection the bias changed: {int(np.any(unbiased != idx, axis=1).sum())}; "
+        f"y err {err:.3g}")
+
+
+@pytest.mark.parametrize("name,gamma", [("S_capgate", 0.5), ("S_rankcap", 0.5)])
+def test_bias_controller_trajectory(name, gamma):
+    """Twelve feedback windows of two forwards each: counts accumulate on the device,
+    moe_bias_update applies Eq. 37 and resets them. The selections, window counts and
+    the whole bias trajectory match the oracle bit for bit, and the requested max/mean
+    imbalance falls."""
+    L = DeviceLayer(synth.get_config(name))
+    c = L.cfg
+    b = torch.zeros(c.N, dtype=torch.float32, device="cuda")
+    acc = torch.zeros(c.N, dtype=torch.int32, device="cuda")
+    lay = moe.MoELayer(L.x, L.w_router, L.w_gate, L.w_up, L.w_down, c.K, keep_intermediates=True,
+                       expert_bias=b, count_accum=acc, **L.layer_kwargs())
+    b_ref = np.zeros(c.N, dtype=np.float32)
+    imax = []
+    for step in range(12):
+        for _ in range(2):
+            lay.forward()
+        torch.cuda.synchronize()
+        z = host(lay.out["logits"])
+        idx_ref = O.topk_select(O.selection_keys(z, c.score, b_ref), c.K)
+        assert np.array_equal(host(lay.out["topk_idx"]), idx_ref), f"window {step}"
+        C = 2 * O.requested_counts(idx_ref, c.N)
+        assert np.array_equal(host(acc), C), f"window {step}"
+        imax.append(O.imbalance_max(C))
+        moe.moe_bias_update(acc, b, gamma, reset=True)
+        torch.cuda.synchronize()
+        b_ref = O.bias_update(b_ref, C, gamma)
+        assert np.array_equal(host(b).view(np.int32), b_ref.view(np.int32)), f"window {step}"
+        assert not host(acc).any()
+    say(f"  {name}: requested I_max by window {[round(v, 2) for v in imax]}")
+    assert imax[-1] < 0.6 * imax[0]          # strongly Zipf-skewed start: I_max = N / K

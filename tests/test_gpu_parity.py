@@ -442,7 +442,8 @@ def test_forward_edge_cases():
     # T = 0: nothing enqueued, status OK
     x0 = L.x[:0]
     st = moe.lib.moe_route(0, cfg.d_model, cfg.N, cfg.K, 0, 1, 1.0, 1, x0.data_ptr() or 1,
-                           L.w_router.data_ptr(), None, None, None, 0, 1, 1, None, None, None, 0, None)
+                           L.w_router.data_ptr(), None, None, None, None, 0, 1, 1, None, None, None,
+                           0, None)
     assert st == moe.MOE_OK
 
 
