@@ -209,6 +209,25 @@ def main():
         o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
         reps)
 
+    # next rows on the same batch: balance statistics, rank-wide capacity (8 destinations
+    # of N/8 experts, capacity factor 1), biased selection and the bias controller
+    nx = {}
+    z_l = o["logits"]
+    nx["balance_stats_ms"] = time_graph(torch, lambda: moe.moe_balance_stats(
+        z_l, o["C_req"], o["C_keep"], o["dest_row"], o["topk_r"], score=cfg.score), reps)
+    grp = N // 8 if N % 8 == 0 else N
+    rcap = moe.rank_capacity_from_factor(1.0, K, -(-T // (N // grp)))
+    nx["permute_rank_capacity_ms"] = time_graph(torch, lambda: moe.moe_permute(
+        x, idx, N, rcap, copy_rows=False, capacity_group=grp), reps)
+    eb = torch.linspace(-0.5, 0.5, N, device=x.device, dtype=torch.float32)
+    nx["route_biased_ms"] = time_graph(torch, lambda: moe.moe_route(
+        x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
+        w_shared_gate=gate, want_counts=False, expert_bias=eb), reps)
+    acc = o["C_req"].clone()
+    nx["bias_update_ms"] = time_eager(torch, lambda: moe.moe_bias_update(acc, eb, 1e-3, reset=False),
+                                      reps)
+    nx_bytes = {"balance_stats": T * N * 4 + T * K * 8 + 8 * N}
+
     # algorithmic work (each counted once): flops of the contractions; bytes = weights of
     # the active experts and the shared MLP, x read once, h written once
     act_experts = int((o["C_keep"] > 0).sum().item())
@@ -262,6 +281,9 @@ def main():
                          mfma_frac=round(flops_gateup / t_gateup / 1e12 / PEAK_BF16_TFLOPS, 4)),
         "stages_ms": {k.replace("_ms", ""): round(v, 4) for k, v in st.items()},
         "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
+        "next_rows_ms": {k.replace("_ms", ""): round(v, 4) for k, v in nx.items()},
+        "next_rows_hbm_frac": {"balance_stats": round(
+            nx_bytes["balance_stats"] / (nx["balance_stats_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
     }
     torch.cuda.synchronize()
     if args.copy_probe_mib > 0:

@@ -9,13 +9,16 @@
 // groups of g consecutive experts, also max/mean imbalance of the requested and kept
 // destination totals (Eq. 20-22).
 //
-// stats_partial_kernel: one wave per token, 4 waves per workgroup, TPB tokens per
-// workgroup. A wave normalizes its token's N scores (full softmax of the logits, or
-// sigmoid affinities divided by their sum) with butterfly reductions and adds them to
-// per-lane column sums; lanes k < K count the dropped slots and their coefficients. The
-// four waves' partials are added in a fixed order and written per workgroup.
-// stats_final_kernel: one workgroup adds the partials in workgroup order in fp64 and
-// derives every statistic. No atomics: results are bitwise repeatable.
+// stats_partial_kernel: 4 waves per workgroup, `tpb` tokens per workgroup (16 or more,
+// chosen so that at most 128 workgroups write partials). A wave loads four tokens' logits
+// at once, normalizes each token's N scores (full softmax of the logits, or sigmoid
+// affinities divided by their sum) with butterfly reductions and adds them to per-lane
+// column sums; lanes k < K accumulate the dropped slots and their coefficients. The four
+// waves' partials are added in a fixed order and written per workgroup.
+// stats_final_kernel: 1024 threads add the partials column by column (threads split the
+// workgroups of each expert, eight independent loads in flight, then a fixed-order sum in
+// fp64); wave 0 then derives every statistic with fp64 butterfly reductions over the
+// experts. No atomics: results are bitwise repeatable.
 #include <cmath>
 
 #include "../../include/moe.h"
@@ -26,8 +29,9 @@ using namespace moe;
 namespace {
 
 constexpr int ST_WAVES = 4;
-constexpr int ST_TPB = 64;           // tokens per workgroup
-constexpr int ST_COLS = kMaxN / kWave;  // score columns per lane
+constexpr int ST_BATCH = 4;              // tokens a wave loads at once
+constexpr int ST_MAXBLK = 128;           // partial workgroups at most
+constexpr int ST_COLS = kMaxN / kWave;   // score columns per lane
 
 __device__ __forceinline__ float st_wave_max(float v) {
 #pragma unroll
@@ -39,67 +43,93 @@ __device__ __forceinline__ float st_wave_sum(float v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
+__device__ __forceinline__ double st_wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ double st_wave_max_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+int stats_tokens_per_block(int T) {
+  int tpb = ST_WAVES * ST_BATCH;
+  while ((T + tpb - 1) / tpb > ST_MAXBLK) tpb *= 2;
+  return tpb;
+}
 
 // partial layout per workgroup b: colsum[b][N] (float), then drops[b][4] (float):
 // tokens losing >= 1 route, tokens losing all K, dropped coefficient sum, coefficient sum
 __global__ void __launch_bounds__(ST_WAVES * kWave)
-stats_partial_kernel(int T, int N, int K, int score, const float* __restrict__ logits,
+stats_partial_kernel(int T, int N, int K, int score, int tpb, const float* __restrict__ logits,
                      const int32_t* __restrict__ dest_row, const float* __restrict__ topk_r,
                      float* __restrict__ colsum, float* __restrict__ drops) {
   __shared__ float s_col[ST_WAVES][kMaxN];
   __shared__ float s_drop[ST_WAVES][4];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * ST_TPB;
+  const int t0 = blockIdx.x * tpb;
+  const int t_end = min(T, t0 + tpb);
   float acc[ST_COLS];
 #pragma unroll
   for (int j = 0; j < ST_COLS; ++j) acc[j] = 0.f;
   float lost_any = 0.f, lost_all = 0.f, w_drop = 0.f, w_sel = 0.f;
-  for (int t = t0 + w; t < min(T, t0 + ST_TPB); t += ST_WAVES) {
-    const float* z = logits + static_cast<size_t>(t) * N;
-    float v[ST_COLS];
+  for (int base = t0 + w * ST_BATCH; base < t_end; base += ST_WAVES * ST_BATCH) {
+    float v[ST_BATCH][ST_COLS];
+    int dropped[ST_BATCH];
+    float rk[ST_BATCH];
 #pragma unroll
-    for (int j = 0; j < ST_COLS; ++j) {
-      const int e = lane + j * kWave;
-      v[j] = e < N ? z[e] : -INFINITY;
-    }
-    float sum = 0.f;
-    if (score == MOE_SCORE_SIGMOID) {
-#pragma unroll
-      for (int j = 0; j < ST_COLS; ++j) {
-        const int e = lane + j * kWave;
-        v[j] = e < N ? 1.0f / (1.0f + expf(-v[j])) : 0.f;
-        sum += v[j];
-      }
-    } else {
-      float m = v[0];
-#pragma unroll
-      for (int j = 1; j < ST_COLS; ++j) m = fmaxf(m, v[j]);
-      m = st_wave_max(m);
+    for (int u = 0; u < ST_BATCH; ++u) {  // every load of the batch first
+      const int t = base + u;
+      const bool ok = t < t_end;
+      const float* z = logits + static_cast<size_t>(ok ? t : 0) * N;
 #pragma unroll
       for (int j = 0; j < ST_COLS; ++j) {
         const int e = lane + j * kWave;
-        v[j] = e < N ? expf(v[j] - m) : 0.f;
-        sum += v[j];
+        v[u][j] = (ok && e < N) ? z[e] : -INFINITY;
       }
+      const bool slot = ok && lane < K;
+      const size_t tk = static_cast<size_t>(ok ? t : 0) * K + lane;
+      dropped[u] = slot ? (dest_row[tk] < 0) : 0;
+      rk[u] = slot ? topk_r[tk] : 0.f;
     }
-    const float inv = 1.0f / st_wave_sum(sum);
 #pragma unroll
-    for (int j = 0; j < ST_COLS; ++j) acc[j] += v[j] * inv;
-    // dropped slots of this token (lanes k < K)
-    int dropped = 0;
-    float rk = 0.f;
-    if (lane < K) {
-      const size_t tk = static_cast<size_t>(t) * K + lane;
-      dropped = dest_row[tk] < 0;
-      rk = topk_r[tk];
+    for (int u = 0; u < ST_BATCH; ++u) {
+      if (base + u >= t_end) break;  // uniform across the wave
+      float sum = 0.f;
+      if (score == MOE_SCORE_SIGMOID) {
+#pragma unroll
+        for (int j = 0; j < ST_COLS; ++j) {
+          const int e = lane + j * kWave;
+          v[u][j] = e < N ? 1.0f / (1.0f + expf(-v[u][j])) : 0.f;
+          sum += v[u][j];
+        }
+      } else {
+        float m = v[u][0];
+#pragma unroll
+        for (int j = 1; j < ST_COLS; ++j) m = fmaxf(m, v[u][j]);
+        m = st_wave_max(m);
+#pragma unroll
+        for (int j = 0; j < ST_COLS; ++j) {
+          const int e = lane + j * kWave;
+          v[u][j] = e < N ? expf(v[u][j] - m) : 0.f;
+          sum += v[u][j];
+        }
+      }
+      const float inv = 1.0f / st_wave_sum(sum);
+#pragma unroll
+      for (int j = 0; j < ST_COLS; ++j) acc[j] += v[u][j] * inv;
+      const int nd = __popcll(__ballot(dropped[u]));
+      lost_any += nd > 0 ? 1.f : 0.f;
+      lost_all += nd == K ? 1.f : 0.f;
+      w_drop += dropped[u] ? rk[u] : 0.f;
+      w_sel += rk[u];
     }
-    const int nd = __popcll(__ballot(dropped));
-    lost_any += nd > 0 ? 1.f : 0.f;
-    lost_all += nd == K ? 1.f : 0.f;
-    w_drop += st_wave_sum(dropped ? rk : 0.f);
-    w_sel += st_wave_sum(rk);
   }
+  w_drop = st_wave_sum(w_drop);
+  w_sel = st_wave_sum(w_sel);
 #pragma unroll
   for (int j = 0; j < ST_COLS; ++j) {
     const int e = lane + j * kWave;
@@ -126,86 +156,113 @@ stats_partial_kernel(int T, int N, int K, int score, const float* __restrict__ l
   }
 }
 
-constexpr int SF_THREADS = 256;
-
-// fixed-order tree sum / max over the workgroup (fp64)
-__device__ double sf_sum(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int off = SF_THREADS / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
-}
-__device__ double sf_max(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int off = SF_THREADS / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmax(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
-}
+constexpr int SF_THREADS = 1024;
 
 __global__ void __launch_bounds__(SF_THREADS)
-stats_final_kernel(int T, int N, int K, int group, int nblk, const float* __restrict__ colsum,
-                   const float* __restrict__ drops, const int32_t* __restrict__ C_req,
-                   const int32_t* __restrict__ C_keep, float* __restrict__ P_out,
-                   float* __restrict__ stats) {
-  __shared__ double red[SF_THREADS];
-  __shared__ double s_req[SF_THREADS], s_keep[SF_THREADS];
+stats_final_kernel(int T, int N, int K, int group, int nblk, int NP,
+                   const float* __restrict__ colsum, const float* __restrict__ drops,
+                   const int32_t* __restrict__ C_req, const int32_t* __restrict__ C_keep,
+                   float* __restrict__ P_out, float* __restrict__ stats) {
+  __shared__ double part[SF_THREADS];
+  __shared__ double dpart[64];
+  __shared__ double s_P[kMaxN], s_req[kMaxN], s_keep[kMaxN];
   const int tid = threadIdx.x;
-  const double KT = static_cast<double>(K) * T;
-  // P_i and per-expert terms (N <= 256: one expert per thread)
-  double P = 0.0, creq = 0.0, ckeep = 0.0;
-  const bool act = tid < N;
-  if (act) {
-    for (int b = 0; b < nblk; ++b) P += colsum[static_cast<size_t>(b) * N + tid];
+  // column sums: thread (e, q) adds workgroups [q per, (q+1) per) of expert e
+  {
+    const int Q = SF_THREADS / NP;
+    const int e = tid % NP, q = tid / NP;
+    const int per = (nblk + Q - 1) / Q;
+    const int b0 = min(q * per, nblk), b1 = min(b0 + per, nblk);
+    double acc = 0.0;
+    if (e < N) {
+      int b = b0;
+      for (; b + 8 <= b1; b += 8) {
+        float h[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h[u] = colsum[static_cast<size_t>(b + u) * N + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += h[u];
+      }
+      for (; b < b1; ++b) acc += colsum[static_cast<size_t>(b) * N + e];
+    }
+    part[tid] = acc;
+  }
+  // drop partials: 16 runs of workgroups for each of the 4 values
+  if (tid < 64) {
+    const int v = tid & 3, q = tid >> 2;
+    const int per = (nblk + 15) / 16;
+    const int b0 = min(q * per, nblk), b1 = min(b0 + per, nblk);
+    double acc = 0.0;
+    for (int b = b0; b < b1; ++b) acc += drops[b * 4 + v];
+    dpart[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < N) {
+    const int Q = SF_THREADS / NP;
+    double P = 0.0;
+    for (int q = 0; q < Q; ++q) P += part[q * NP + tid];  // fixed order
     P /= T;
-    creq = C_req[tid];
-    ckeep = C_keep[tid];
+    s_P[tid] = P;
+    s_req[tid] = C_req[tid];
+    s_keep[tid] = C_keep[tid];
     P_out[tid] = static_cast<float>(P);
   }
-  const double f = creq / KT;
-  const double lbl = N * sf_sum(act ? f * P : 0.0, red);
-  const double sreq = sf_sum(creq, red), skeep = sf_sum(ckeep, red);
-  const double mreq = sf_max(act ? creq : 0.0, red), mkeep = sf_max(act ? ckeep : 0.0, red);
-  const double never = sf_sum(act && creq == 0.0 ? 1.0 : 0.0, red);
-  auto plogp = [](double x, double tot) { return x > 0.0 ? (x / tot) * log(x / tot) : 0.0; };
-  const double hreq = sreq > 0 ? -sf_sum(act ? plogp(creq, sreq) : 0.0, red) : 0.0;
-  const double hkeep = skeep > 0 ? -sf_sum(act ? plogp(ckeep, skeep) : 0.0, red) : 0.0;
+  __syncthreads();
+  if (tid >= kWave) return;
+  // wave 0: lane l owns experts l, l + 64, ...
+  const int lane = tid;
+  const double KT = static_cast<double>(K) * T;
+  double fP = 0.0, sreq = 0.0, skeep = 0.0, never = 0.0, mreq = 0.0, mkeep = 0.0;
+  for (int e = lane; e < N; e += kWave) {
+    fP += s_req[e] / KT * s_P[e];
+    sreq += s_req[e];
+    skeep += s_keep[e];
+    never += s_req[e] == 0.0 ? 1.0 : 0.0;
+    mreq = fmax(mreq, s_req[e]);
+    mkeep = fmax(mkeep, s_keep[e]);
+  }
+  fP = st_wave_sum_d(fP);
+  sreq = st_wave_sum_d(sreq);
+  skeep = st_wave_sum_d(skeep);
+  never = st_wave_sum_d(never);
+  mreq = st_wave_max_d(mreq);
+  mkeep = st_wave_max_d(mkeep);
   const double mean_req = sreq / N, mean_keep = skeep / N;
-  const double vreq = sf_sum(act ? (creq - mean_req) * (creq - mean_req) : 0.0, red) / N;
-  const double vkeep = sf_sum(act ? (ckeep - mean_keep) * (ckeep - mean_keep) : 0.0, red) / N;
-  // destination totals R_q (thread q < N / group sums its group's experts in order)
-  s_req[tid] = creq;
-  s_keep[tid] = ckeep;
-  __syncthreads();
+  double hreq = 0.0, hkeep = 0.0, vreq = 0.0, vkeep = 0.0;
+  for (int e = lane; e < N; e += kWave) {
+    if (s_req[e] > 0.0) hreq -= (s_req[e] / sreq) * log(s_req[e] / sreq);
+    if (s_keep[e] > 0.0) hkeep -= (s_keep[e] / skeep) * log(s_keep[e] / skeep);
+    vreq += (s_req[e] - mean_req) * (s_req[e] - mean_req);
+    vkeep += (s_keep[e] - mean_keep) * (s_keep[e] - mean_keep);
+  }
+  hreq = st_wave_sum_d(hreq);
+  hkeep = st_wave_sum_d(hkeep);
+  vreq = st_wave_sum_d(vreq) / N;
+  vkeep = st_wave_sum_d(vkeep) / N;
+  // destination totals R_q: lane l sums destinations l, l + 64, ... (experts in order)
   const int M = group > 0 ? N / group : 0;
-  double rreq = 0.0, rkeep = 0.0;
-  if (tid < M)
-    for (int j = tid * group; j < (tid + 1) * group; ++j) {
-      rreq += s_req[j];
-      rkeep += s_keep[j];
+  double mrreq = 0.0, mrkeep = 0.0;
+  for (int q = lane; q < M; q += kWave) {
+    double rq = 0.0, rk = 0.0;
+    for (int j = q * group; j < (q + 1) * group; ++j) {
+      rq += s_req[j];
+      rk += s_keep[j];
     }
-  const double mrreq = sf_max(rreq, red), mrkeep = sf_max(rkeep, red);
-  // drop partials, in workgroup order
-  double d[4] = {0.0, 0.0, 0.0, 0.0};
-  if (tid < 4)
-    for (int b = 0; b < nblk; ++b) d[tid] += drops[b * 4 + tid];
-  red[tid] = tid < 4 ? d[tid] : 0.0;
-  __syncthreads();
-  if (tid == 0) {
+    mrreq = fmax(mrreq, rq);
+    mrkeep = fmax(mrkeep, rk);
+  }
+  mrreq = st_wave_max_d(mrreq);
+  mrkeep = st_wave_max_d(mrkeep);
+  double d[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    d[v] = 0.0;
+    for (int q = 0; q < 16; ++q) d[v] += dpart[q * 4 + v];  // fixed order
+  }
+  if (lane == 0) {
     const double nan = __builtin_nan("");
     const double logn = log(static_cast<double>(N));
-    stats[MOE_STAT_LBL] = static_cast<float>(lbl);
+    stats[MOE_STAT_LBL] = static_cast<float>(N * fP);
     stats[MOE_STAT_IMAX_REQ] = static_cast<float>(sreq > 0 ? N * mreq / sreq : nan);
     stats[MOE_STAT_IMAX_KEEP] = static_cast<float>(skeep > 0 ? N * mkeep / skeep : nan);
     // one expert: log N = 0, the load is balanced by construction and the deficit is 0
@@ -215,9 +272,9 @@ stats_final_kernel(int T, int N, int K, int group, int nblk, const float* __rest
     stats[MOE_STAT_CV_KEEP] = static_cast<float>(mean_keep > 0 ? sqrt(vkeep) / mean_keep : nan);
     stats[MOE_STAT_NEVER_SELECTED] = static_cast<float>(never);
     stats[MOE_STAT_DELTA_ROUTE] = static_cast<float>((KT - skeep) / KT);
-    stats[MOE_STAT_TOKENS_LOST_ANY] = static_cast<float>(red[0]);
-    stats[MOE_STAT_TOKENS_LOST_ALL] = static_cast<float>(red[1]);
-    stats[MOE_STAT_WEIGHT_REMOVED] = static_cast<float>(red[3] > 0 ? red[2] / red[3] : nan);
+    stats[MOE_STAT_TOKENS_LOST_ANY] = static_cast<float>(d[0]);
+    stats[MOE_STAT_TOKENS_LOST_ALL] = static_cast<float>(d[1]);
+    stats[MOE_STAT_WEIGHT_REMOVED] = static_cast<float>(d[3] > 0 ? d[2] / d[3] : nan);
     // destination totals sum to the expert totals
     stats[MOE_STAT_IMAX_RANK_REQ] = static_cast<float>(M > 0 && sreq > 0 ? M * mrreq / sreq : nan);
     stats[MOE_STAT_IMAX_RANK_KEEP] = static_cast<float>(M > 0 && skeep > 0 ? M * mrkeep / skeep : nan);
@@ -227,7 +284,8 @@ stats_final_kernel(int T, int N, int K, int group, int nblk, const float* __rest
 }  // namespace
 
 size_t stats_workspace_bytes(int T, int N) {
-  const size_t nblk = (static_cast<size_t>(T) + ST_TPB - 1) / ST_TPB;
+  const int tpb = stats_tokens_per_block(T);
+  const size_t nblk = (static_cast<size_t>(T) + tpb - 1) / tpb;
   return nblk * (static_cast<size_t>(N) + 4) * sizeof(float);
 }
 
@@ -235,12 +293,15 @@ hipError_t launch_balance_stats(int T, int N, int K, int score, int group, const
                                 const int32_t* dest_row, const float* topk_r,
                                 const int32_t* C_req, const int32_t* C_keep, float* P,
                                 float* stats, void* workspace, hipStream_t stream) {
-  const int nblk = (T + ST_TPB - 1) / ST_TPB;
+  const int tpb = stats_tokens_per_block(T);
+  const int nblk = (T + tpb - 1) / tpb;
   float* colsum = static_cast<float*>(workspace);
   float* drops = colsum + static_cast<size_t>(nblk) * N;
+  int NP = 1;
+  while (NP < N) NP <<= 1;
   hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(ST_WAVES * kWave), 0, stream, T, N,
-                     K, score, logits, dest_row, topk_r, colsum, drops);
+                     K, score, tpb, logits, dest_row, topk_r, colsum, drops);
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(SF_THREADS), 0, stream, T, N, K, group,
-                     nblk, colsum, drops, C_req, C_keep, P, stats);
+                     nblk, NP, colsum, drops, C_req, C_keep, P, stats);
   return hipGetLastError();
 }
