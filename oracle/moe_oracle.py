@@ -422,6 +422,76 @@ def shared_output(x, shared_experts: Sequence) -> Optional[np.ndarray]:
 
 
 # ----------------------------------------------------------------------------------------
+# f4: backward of the layer with the routing coefficients held fixed
+# ----------------------------------------------------------------------------------------
+def swiglu_backward(X, w_gate, w_up, w_down, dF):
+    """Chain rule through E(X) = [SiLU(X W_g) * (X W_u)] W_d (p4 Eq. 74) for an upstream
+    gradient dF of its output: with A = X W_g, B = X W_u, S = SiLU(A), H = S * B,
+      dH = dF W_d^T,  dB = dH * S,  dA = dH * B * SiLU'(A),  SiLU'(a) = s(a)(1 + a(1 - s(a))),
+      dX = dA W_g^T + dB W_u^T,  dW_g = X^T dA,  dW_u = X^T dB,  dW_d = H^T dF,
+    returned in the stored-transposed layouts of the weights: (dX, dw_gate [d_ff, d_model],
+    dw_up [d_ff, d_model], dw_down [d_model, d_ff])."""
+    X, dF = _f64(X), _f64(dF)
+    Wg, Wu, Wd = _f64(w_gate), _f64(w_up), _f64(w_down)
+    A = X @ Wg.T
+    B = X @ Wu.T
+    sg = _sigmoid(A)
+    S = A * sg
+    H = S * B
+    dH = dF @ Wd
+    dB = dH * S
+    dA = dH * B * sg * (1.0 + A * (1.0 - sg))
+    dX = dA @ Wg + dB @ Wu
+    return dX, dA.T @ X, dB.T @ X, dF.T @ H
+
+
+@dataclass
+class Gradients:
+    dx: np.ndarray                # [T, d_model]
+    dw_gate: np.ndarray           # [N, d_r, d_model]
+    dw_up: np.ndarray             # [N, d_r, d_model]
+    dw_down: np.ndarray           # [N, d_model, d_r]
+    shared: list                  # per shared expert: (dw_gate, dw_up, dw_down)
+
+
+def backward(x, idx, kept, r, expert_weights: Callable[[int], tuple], N: int, dy,
+             shared_experts: Sequence = (), s=1.0) -> Gradients:
+    """Gradients of the layer output y (p1 Eq. 80) for an upstream gradient dy, with the
+    router held fixed: the selected experts, the kept routes, the coefficients r and the
+    shared gain s (scalar or per-token gate) are constants (the fixed-router input
+    gradient of p1 Section 21.3). Expert i's output row of kept route (t, i) receives
+    r_{t,i} dy_t; each expert's rows are back-propagated through Eq. 74; the input
+    gradient of token t sums its kept routes' rows and the shared branch, which receives
+    s_t dy_t. Experts without kept rows get zero weight gradients."""
+    x, dy = _f64(x), _f64(dy)
+    idx = np.asarray(idx)
+    kept = np.asarray(kept, dtype=bool)
+    r = _f64(r)
+    T, K = idx.shape
+    dx = np.zeros_like(x)
+    dwg = dwu = dwd = None
+    for e in range(N):
+        wg, wu, wd = expert_weights(e)
+        if dwg is None:
+            dwg = np.zeros((N,) + np.shape(wg))
+            dwu = np.zeros((N,) + np.shape(wu))
+            dwd = np.zeros((N,) + np.shape(wd))
+        toks, slots = np.nonzero((idx == e) & kept)      # ascending token order
+        if toks.size == 0:
+            continue
+        dF = r[toks, slots, None] * dy[toks]
+        dX, dwg[e], dwu[e], dwd[e] = swiglu_backward(x[toks], wg, wu, wd, dF)
+        np.add.at(dx, toks, dX)
+    gain = np.broadcast_to(_f64(s), (T,))[:, None]
+    shared = []
+    for (wg, wu, wd) in shared_experts:
+        dX, g1, g2, g3 = swiglu_backward(x, wg, wu, wd, gain * dy)
+        dx += dX
+        shared.append((g1, g2, g3))
+    return Gradients(dx, dwg, dwu, dwd, shared)
+
+
+# ----------------------------------------------------------------------------------------
 # a8: combine
 # ----------------------------------------------------------------------------------------
 def combine(F_perm, dest_row, r, G=None, s=1.0) -> np.ndarray:

@@ -802,3 +802,127 @@ def test_bias_controller_moves_load_toward_balance():
         b = b_new
     C = O.requested_counts(O.topk_select(O.selection_keys(z, O.SOFTMAX, b), K), N)
     assert O.imbalance_max(C) < 0.5 * O.imbalance_max(C0)
+
+
+# ---------------------------------------------------------------------------------------
+# f4: backward with the router held fixed
+# ---------------------------------------------------------------------------------------
+def _small_layer(rng, T=9, d=8, N=4, K=2, d_r=6, shared=(4, 2), drop=True):
+    z = rng.standard_normal((T, N))
+    idx = O.topk_select(z, K)
+    r = O.route_coefficients(z, idx, O.SOFTMAX, True, float(K))
+    kept = O.keep_routes(idx, N, 3 if drop else -1)
+    W = [tuple(rng.standard_normal(sh) * 0.5 for sh in ((d_r, d), (d_r, d), (d, d_r)))
+         for _ in range(N)]
+    S = [tuple(rng.standard_normal(sh) * 0.5 for sh in ((w, d), (w, d), (d, w))) for w in shared]
+    x = rng.standard_normal((T, d))
+    return x, idx, r, kept, W, S
+
+
+def test_backward_matches_finite_differences():
+    """The fixed-router backward against central differences of the oracle's own
+    forward with the routing held fixed (p1 Eq. 80 with p4 Eq. 74): for a random
+    direction V of x or of any weight, <dL/dtheta, V> = (L(theta + hV) - L(theta - hV)) / 2h
+    with L = <dy, y>. Capacity drops some routes; the shared gain is a per-token gate."""
+    rng = np.random.default_rng(21)
+    x, idx, r, kept, W, S = _small_layer(rng)
+    T, N, K = x.shape[0], len(W), idx.shape[1]
+    assert not kept.all()
+    s_tok = rng.uniform(0.2, 0.9, T)
+    dy = rng.standard_normal(x.shape)
+    spec = O.LayerSpec(N=N, K=K)
+
+    def loss(xx, WW, SS):
+        y = O.forward_tokens(spec, range(T), xx, idx, r, kept, lambda e: WW[e], SS, s_tok)
+        return float((dy * y).sum())
+
+    g = O.backward(x, idx, kept, r, lambda e: W[e], N, dy, S, s_tok)
+    h = 1e-6
+
+    def check(analytic, perturb):
+        V = rng.standard_normal(analytic.shape)
+        fd = (perturb(h * V) - perturb(-h * V)) / (2 * h)
+        assert abs(fd - float((analytic * V).sum())) <= 1e-6 * max(1.0, abs(fd))
+
+    check(g.dx, lambda dV: loss(x + dV, W, S))
+    for e in range(N):
+        for j, name in enumerate(("dw_gate", "dw_up", "dw_down")):
+            def pert(dV, e=e, j=j):
+                WW = [list(w) for w in W]
+                WW[e][j] = WW[e][j] + dV
+                return loss(x, [tuple(w) for w in WW], S)
+            check(getattr(g, name)[e], pert)
+    for q in range(len(S)):
+        for j in range(3):
+            def pert(dV, q=q, j=j):
+                SS = [list(w) for w in S]
+                SS[q][j] = SS[q][j] + dV
+                return loss(x, W, [tuple(w) for w in SS])
+            check(g.shared[q][j], pert)
+
+
+def test_backward_dense_special_case_autograd():
+    """p1 Eq. 81 and the slice-by-slice mapping of parameter gradients (p4): with unit
+    coefficients and every token selecting the same K experts (all kept), the layer is a
+    dense SwiGLU MLP of width K d_r + d_s; the oracle's gradients equal torch autograd's
+    (float64, CPU) on that dense MLP, slice by slice."""
+    import torch
+    rng = np.random.default_rng(3)
+    T, d, N, K, d_r, d_s = 6, 8, 5, 3, 4, 2
+    z = np.tile(np.array([0.5, 3.0, -1.0, 2.0, 1.0]), (T, 1))   # every token picks 1, 3, 4
+    idx = O.topk_select(z, K)
+    kept = np.ones((T, K), bool)
+    r = np.ones((T, K))
+    W = [tuple(rng.standard_normal(sh) for sh in ((d_r, d), (d_r, d), (d, d_r))) for _ in range(N)]
+    S = [tuple(rng.standard_normal(sh) for sh in ((d_s, d), (d_s, d), (d, d_s)))]
+    x, dy = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    g = O.backward(x, idx, kept, r, lambda e: W[e], N, dy, S, 1.0)
+    sel = list(idx[0])
+    parts = [W[e] for e in sel] + S
+    tg = torch.tensor(np.concatenate([p[0] for p in parts]), requires_grad=True)
+    tu = torch.tensor(np.concatenate([p[1] for p in parts]), requires_grad=True)
+    td = torch.tensor(np.concatenate([p[2] for p in parts], axis=1), requires_grad=True)
+    tx = torch.tensor(x, requires_grad=True)
+    y = (torch.nn.functional.silu(tx @ tg.T) * (tx @ tu.T)) @ td.T
+    (y * torch.tensor(dy)).sum().backward()
+    assert np.allclose(g.dx, tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+    for j, e in enumerate(sel):
+        sl = slice(j * d_r, (j + 1) * d_r)
+        assert np.allclose(g.dw_gate[e], tg.grad.numpy()[sl], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g.dw_up[e], tu.grad.numpy()[sl], rtol=1e-12, atol=1e-12)
+        assert np.allclose(g.dw_down[e], td.grad.numpy()[:, sl], rtol=1e-12, atol=1e-12)
+    sl = slice(K * d_r, K * d_r + d_s)
+    assert np.allclose(g.shared[0][0], tg.grad.numpy()[sl], rtol=1e-12, atol=1e-12)
+    assert np.allclose(g.shared[0][2], td.grad.numpy()[:, sl], rtol=1e-12, atol=1e-12)
+    for e in set(range(N)) - set(sel):
+        assert not g.dw_gate[e].any() and not g.dw_down[e].any()
+
+
+def test_fig70c_down_weight_gradient_ratios():
+    """p1 Figure 70(c) with the Table 37 conventions: for the same upstream gradient and
+    a fixed router, the routed and shared down-projection gradients scale with the
+    routed coefficient factor (relative to K p) and with s; the printed ratios follow at
+    the surrogate's width ratio d_r : d_s = 2 : 1 with K = 4."""
+    with open(os.path.join(GOLD, "fig70c_down_weight_grad_ratios.json")) as f:
+        gold = json.load(f)
+    K, d_r_fig, d_s_fig = gold["K"], gold["d_r"], gold["d_s"]
+    rng = np.random.default_rng(70)
+    T, d, N, d_r, d_s = 24, 10, 6, 8, 4          # same d_r : d_s ratio, smaller
+    d_act = K * d_r + d_s
+    assert d_r * (K * d_r_fig + d_s_fig) == d_r_fig * d_act
+    z = rng.standard_normal((T, N))
+    idx = O.topk_select(z, K)
+    p = O.route_coefficients(z, idx, O.SOFTMAX, True, 1.0)     # selected p, sum 1
+    kept = np.ones((T, K), bool)
+    W = [tuple(rng.standard_normal(sh) * 0.3 for sh in ((d_r, d), (d_r, d), (d, d_r))) for _ in range(N)]
+    S = [tuple(rng.standard_normal(sh) * 0.3 for sh in ((d_s, d), (d_s, d), (d, d_s)))]
+    x, dy = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    conv = {"olmo": (K, 1.0), "routed_unit_sum": (1.0, 1.0), "equal_branch_mass": (0.5, 0.5),
+            "width_proportional_unit_sum": (K * d_r / d_act, d_s / d_act)}
+    rms = lambda a: float(np.sqrt(np.mean(np.square(a))))
+    g = {k: O.backward(x, idx, kept, c * p, lambda e: W[e], N, dy, S, sv) for k, (c, sv) in conv.items()}
+    for k, want in gold["ratios"].items():
+        routed = rms(g[k].dw_down) / rms(g["olmo"].dw_down)
+        shared = rms(g[k].shared[0][2]) / rms(g["olmo"].shared[0][2])
+        assert round(routed, 3) == want["routed_down"], (k, routed)
+        assert round(shared, 3) == want["shared_down"], (k, shared)
