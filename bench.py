@@ -227,6 +227,19 @@ def main():
     nx["bias_update_ms"] = time_eager(torch, lambda: moe.moe_bias_update(acc, eb, 1e-3, reset=False),
                                       reps)
     nx_bytes = {"balance_stats": T * N * 4 + T * K * 8 + 8 * N}
+    # f4: fixed-router backward on the same batch (recompute A, B; dH; dX; weight gradients)
+    bwd_flops = None
+    if dt == "bf16":
+        layer_t = moe.MoELayer(x, w_router, w_gate, w_up, w_down, K, score=cfg.score,
+                               renorm=cfg.renorm, alpha=cfg.alpha, s=cfg.s, capacity=cap,
+                               logit_bias=bias, w_shared_gate=gate, shared=shared, trainable=True)
+        layer_t.forward()
+        dy = torch.randn(T, d, device=x.device, dtype=torch.float32).to(torch.bfloat16)
+        nx["backward_ms"] = time_eager(torch, lambda: layer_t.backward(dy), max(3, reps // 4))
+        R_t = int(layer_t.out["offsets"][-1].item())
+        bwd_flops = 16.0 * R_t * d * d_r + 16.0 * T * d * (layer_t.shared_mlp[0].shape[0]
+                                                           if layer_t.shared_mlp else 0)
+        del layer_t
 
     # algorithmic work (each counted once): flops of the contractions; bytes = weights of
     # the active experts and the shared MLP, x read once, h written once
@@ -282,6 +295,8 @@ def main():
         "stages_ms": {k.replace("_ms", ""): round(v, 4) for k, v in st.items()},
         "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
         "next_rows_ms": {k.replace("_ms", ""): round(v, 4) for k, v in nx.items()},
+        "backward_tflops": (round(bwd_flops / (nx["backward_ms"] * 1e-3) / 1e12, 1)
+                            if bwd_flops else None),
         "next_rows_hbm_frac": {"balance_stats": round(
             nx_bytes["balance_stats"] / (nx["balance_stats_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
     }

@@ -392,6 +392,69 @@ size_t moe_forward_workspace_size(const moe_forward_args* args);
 int moe_forward(const moe_forward_args* args, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------
+ * moe_pack_weights_transposed: packs the transpose of a stack of two matrices in the
+ * moe_pack_weights operand order, for the backward's data-gradient contractions:
+ *   Wt[g][n][k] = k < K_a ? w_a[g][k][n] : w_b[g][k - K_a][n],   n < N_dim, k < K_dim
+ * w_a is [G][K_a][N_dim] and w_b [G][K_dim - K_a][N_dim] (NULL when K_a = K_dim), all bf16
+ * device memory; dst is [G][N_dim][K_dim] packed (same size) and must not overlap them.
+ * Backward operands: pack(w_down^T) with w_a = w_down viewed [G][d_model][d_r] gives the
+ * [G][d_r][d_model] operand of dH; w_a = w_gate, w_b = w_up ([G][d_r][d_model] each) give
+ * the [G][d_model][2 d_r] operand of dX. N_dim, K_dim, K_a multiples of 64 (else
+ * MOE_ERR_UNSUPPORTED); bf16 only.
+ * ------------------------------------------------------------------------------- */
+int moe_pack_weights_transposed(int G, int N_dim, int K_dim, int K_a, int dt, const void* w_a,
+                                const void* w_b, void* dst, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_backward: gradients of the layer output y (Section 21 Eq. 80 with Section 20
+ * Eq. 74 experts) for an upstream gradient dy, with the router held fixed (the
+ * fixed-router gradients of Section 21.3): the selection, the kept routes, r and the
+ * shared gain are the forward's and are treated as constants. Each kept route's expert
+ * row receives r dy and the shared MLP s dy; with A = X W_g^T, B = X W_u^T (recomputed),
+ *   dH = dF W_d, dA = dH * B * SiLU'(A), dB = dH * SiLU(A), dX = dA W_g + dB W_u,
+ *   dW_d = dF^T H, dW_g = dA^T X, dW_u = dB^T X,
+ * and dx sums each token's kept routes' dX rows and the shared branch's. Experts with
+ * no kept row get zero weight gradients. bf16 activations and weights (fp32
+ * accumulation); weight gradients are written in fp32. Everything is enqueued on
+ * `stream` without host synchronization.
+ * Returns MOE_ERR_UNSUPPORTED unless dt = MOE_BF16 and the forward's size limits hold,
+ * MOE_ERR_INVALID_ARG for a NULL required pointer or inconsistent sizes,
+ * MOE_ERR_WORKSPACE for a short workspace; T = 0 enqueues nothing.
+ * ------------------------------------------------------------------------------- */
+typedef struct moe_backward_args {
+  int T, d_model, N, K, d_r, d_s;
+  int dt;                     /* MOE_BF16 */
+  float s;                    /* shared gain when s_tok == NULL */
+  int max_rows;               /* rows of the forward's packed buffers (moe_max_rows) */
+  const void* x;              /* [T][d_model] the forward's input */
+  const void* dy;             /* [T][d_model] upstream gradient */
+  const int32_t* row_token;   /* [max_rows] } the forward's routing (moe_permute / */
+  const int32_t* offsets;     /* [N+1]      } moe_forward outputs)                 */
+  const int32_t* dest_row;    /* [T][K]     }                                       */
+  const float* topk_r;        /* [T][K]     }                                       */
+  const float* s_tok;         /* [T] per-token shared gate, or NULL */
+  const void* w_gate;         /* [N][d_r][d_model] packed (moe_pack_weights) */
+  const void* w_up;           /* [N][d_r][d_model] packed */
+  const void* wt_down;        /* [N][d_r][d_model] packed transpose of w_down */
+  const void* wt_gate_up;     /* [N][d_model][2 d_r] packed transpose of [w_gate; w_up] */
+  const void* ws_gate;        /* [d_s][d_model] packed shared MLP (NULL when d_s = 0) */
+  const void* ws_up;          /* [d_s][d_model] packed */
+  const void* wst_down;       /* [d_s][d_model] packed transpose of ws_down */
+  const void* wst_gate_up;    /* [d_model][2 d_s] packed transpose of [ws_gate; ws_up] */
+  void* dx;                   /* [T][d_model] out, bf16 */
+  float* dw_gate;             /* [N][d_r][d_model] out */
+  float* dw_up;               /* [N][d_r][d_model] out */
+  float* dw_down;             /* [N][d_model][d_r] out */
+  float* dws_gate;            /* [d_s][d_model] out (NULL when d_s = 0) */
+  float* dws_up;              /* [d_s][d_model] out */
+  float* dws_down;            /* [d_model][d_s] out */
+} moe_backward_args;
+
+size_t moe_backward_workspace_size(const moe_backward_args* args);
+int moe_backward(const moe_backward_args* args, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

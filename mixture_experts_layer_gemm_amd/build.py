@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_packed.hip", "gemm_stream.hip", "combine.hip",
-           "stats.hip", "bias.hip", "abi.hip"]
+           "stats.hip", "bias.hip", "backward.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -472,4 +472,156 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   return MOE_OK;
 }
 
+// ---- backward ------------------------------------------------------------------------
+namespace {
+
+struct BwdWs {
+  uint16_t *dF, *A, *B, *dH, *dAB, *H, *dXp;          // routed: [rows][...]
+  uint16_t *dG, *As, *Bs, *dHs, *dABs, *Hs, *dXs;     // shared: [T][...]
+};
+
+size_t carve_backward(const moe_backward_args* a, void* ws, BwdWs* out) {
+  Carver c(ws);
+  BwdWs w{};
+  const size_t R = a->max_rows > 0 ? a->max_rows : 0, T = a->T, d = a->d_model;
+  const size_t dr = a->d_r, ds = a->d_s;
+  w.dF = c.take<uint16_t>(R * d);
+  w.A = c.take<uint16_t>(R * dr);
+  w.B = c.take<uint16_t>(R * dr);
+  w.dH = c.take<uint16_t>(R * dr);
+  w.dAB = c.take<uint16_t>(R * 2 * dr);
+  w.H = c.take<uint16_t>(R * dr);
+  w.dXp = c.take<uint16_t>(R * d);
+  if (ds > 0) {
+    w.dG = c.take<uint16_t>(T * d);
+    w.As = c.take<uint16_t>(T * ds);
+    w.Bs = c.take<uint16_t>(T * ds);
+    w.dHs = c.take<uint16_t>(T * ds);
+    w.dABs = c.take<uint16_t>(T * 2 * ds);
+    w.Hs = c.take<uint16_t>(T * ds);
+    w.dXs = c.take<uint16_t>(T * d);
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+// one plain (no SwiGLU) contraction for the routed experts and, when given, the shared
+// MLP: a single persistent launch when both fit it, else one pass each
+hipError_t plain_pair(const StreamProblem& p0, const StreamProblem* p1, hipStream_t stream) {
+  if (p1 != nullptr && p0.rows > 0 && stream_gemm_supported(false, p0, *p1))
+    return launch_stream_gemm(false, p0, *p1, stream);
+  hipError_t e = hipSuccess;
+  if (p0.rows > 0)
+    e = gemm_pass(false, true, p0.G, p0.Kd, p0.Nd, MOE_BF16, p0.a, p0.a_rows, p0.row_index,
+                  p0.offsets, p0.rows, p0.w0, nullptr, p0.out, stream);
+  if (e == hipSuccess && p1 != nullptr)
+    e = gemm_pass(false, true, 1, p1->Kd, p1->Nd, MOE_BF16, p1->a, p1->a_rows, nullptr, nullptr,
+                  p1->rows, p1->w0, nullptr, p1->out, stream);
+  return e;
+}
+
+}  // namespace
+
+int moe_pack_weights_transposed(int G, int N_dim, int K_dim, int K_a, int dt, const void* w_a,
+                                const void* w_b, void* dst, hipStream_t stream) {
+  MOE_TRY(check_dtype(dt));
+  if (G <= 0 || N_dim <= 0 || K_dim <= 0 || K_a <= 0 || K_a > K_dim || !w_a || !dst)
+    return MOE_ERR_INVALID_ARG;
+  if ((K_a < K_dim) != (w_b != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16 || N_dim % 64 != 0 || K_dim % 64 != 0 || K_a % 64 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t out_bytes = static_cast<size_t>(G) * N_dim * K_dim * 2;
+  const size_t a_bytes = static_cast<size_t>(G) * K_a * N_dim * 2;
+  const size_t b_bytes = static_cast<size_t>(G) * (K_dim - K_a) * N_dim * 2;
+  const char* o = static_cast<const char*>(dst);
+  const char* pa = static_cast<const char*>(w_a);
+  const char* pb = static_cast<const char*>(w_b);
+  if (pa < o + out_bytes && o < pa + a_bytes) return MOE_ERR_INVALID_ARG;  // overlap
+  if (pb && pb < o + out_bytes && o < pb + b_bytes) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_transpose_pack(G, N_dim, K_dim, K_a, w_a, w_b, dst, stream));
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_size(const moe_backward_args* a) {
+  if (!a || a->T <= 0 || a->d_model <= 0 || a->d_r <= 0 || a->d_s < 0) return 0;
+  return carve_backward(a, nullptr, nullptr);
+}
+
+int moe_backward(const moe_backward_args* a, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_router_dims(a->T, a->d_model, a->N, a->K));
+  MOE_TRY(check_dtype(a->dt));
+  if (a->dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (a->d_r <= 0 || a->d_s < 0 || a->max_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (a->d_r % 64 != 0 || a->d_s % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!a->x || !a->dy || !a->row_token || !a->offsets || !a->dest_row || !a->topk_r ||
+      !a->w_gate || !a->w_up || !a->wt_down || !a->wt_gate_up || !a->dx || !a->dw_gate ||
+      !a->dw_up || !a->dw_down)
+    return MOE_ERR_INVALID_ARG;
+  if (a->d_s > 0 && (!a->ws_gate || !a->ws_up || !a->wst_down || !a->wst_gate_up ||
+                     !a->dws_gate || !a->dws_up || !a->dws_down))
+    return MOE_ERR_INVALID_ARG;
+  if (a->max_rows > static_cast<long>(a->K) * a->T) return MOE_ERR_INVALID_ARG;
+  if (a->T == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < moe_backward_workspace_size(a)) return MOE_ERR_WORKSPACE;
+  BwdWs w{};
+  carve_backward(a, workspace, &w);
+  const int T = a->T, d = a->d_model, N = a->N, K = a->K, dr = a->d_r, ds = a->d_s;
+  const int R = a->max_rows;
+  const bool sh = ds > 0;
+  // upstream rows: dF = r dy in the packed expert order, dG = s dy
+  MOE_HIP(launch_grad_rows(T, d, K, a->dy, a->dest_row, a->topk_r, a->s, a->s_tok, w.dF,
+                           sh ? w.dG : nullptr, stream));
+  // recompute A and B (rows gathered from x, as in the forward)
+  {
+    const StreamProblem pa = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_gate,
+                                     nullptr, w.A);
+    const StreamProblem pas = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_gate, nullptr,
+                                      w.As);
+    MOE_HIP(plain_pair(pa, sh ? &pas : nullptr, stream));
+    const StreamProblem pb = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_up,
+                                     nullptr, w.B);
+    const StreamProblem pbs = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_up, nullptr,
+                                      w.Bs);
+    MOE_HIP(plain_pair(pb, sh ? &pbs : nullptr, stream));
+  }
+  // dH = dF W_d
+  {
+    const StreamProblem p0 = problem(w.dF, R, nullptr, a->offsets, N, R, d, dr, a->wt_down,
+                                     nullptr, w.dH);
+    const StreamProblem p1 = problem(w.dG, T, nullptr, nullptr, 1, T, d, ds, a->wst_down, nullptr,
+                                     w.dHs);
+    MOE_HIP(plain_pair(p0, sh ? &p1 : nullptr, stream));
+  }
+  // SwiGLU backward: [dA | dB] and H
+  if (R > 0)
+    MOE_HIP(launch_swiglu_bwd(R, a->offsets + N, dr, w.dH, w.A, w.B, w.dAB, w.H, stream));
+  if (sh) MOE_HIP(launch_swiglu_bwd(T, nullptr, ds, w.dHs, w.As, w.Bs, w.dABs, w.Hs, stream));
+  // dX = [dA dB] [W_g; W_u], then dx = sum over kept routes + shared
+  {
+    const StreamProblem p0 = problem(w.dAB, R, nullptr, a->offsets, N, R, 2 * dr, d,
+                                     a->wt_gate_up, nullptr, w.dXp);
+    const StreamProblem p1 = problem(w.dABs, T, nullptr, nullptr, 1, T, 2 * ds, d,
+                                     a->wst_gate_up, nullptr, w.dXs);
+    MOE_HIP(plain_pair(p0, sh ? &p1 : nullptr, stream));
+  }
+  MOE_HIP(launch_combine(T, d, K, MOE_BF16, w.dXp, a->dest_row, nullptr, sh ? w.dXs : nullptr,
+                         1.0f, nullptr, a->dx, stream));
+  // weight gradients, contracting over each expert's rows (zero for experts without rows)
+  MOE_HIP(launch_wgrad(N, d, dr, w.dF, d, w.H, dr, nullptr, a->offsets, R, a->dw_down, stream));
+  MOE_HIP(launch_wgrad(N, dr, d, w.dAB, 2 * dr, a->x, d, a->row_token, a->offsets, R, a->dw_gate,
+                       stream));
+  MOE_HIP(launch_wgrad(N, dr, d, w.dAB + dr, 2 * dr, a->x, d, a->row_token, a->offsets, R,
+                       a->dw_up, stream));
+  if (sh) {
+    MOE_HIP(launch_wgrad(1, d, ds, w.dG, d, w.Hs, ds, nullptr, nullptr, T, a->dws_down, stream));
+    MOE_HIP(launch_wgrad(1, ds, d, w.dABs, 2 * ds, a->x, d, nullptr, nullptr, T, a->dws_gate,
+                         stream));
+    MOE_HIP(launch_wgrad(1, ds, d, w.dABs + ds, 2 * ds, a->x, d, nullptr, nullptr, T, a->dws_up,
+                         stream));
+  }
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,365 @@
+// Backward of the layer with the router held fixed ("Section 21: Merging Routed and
+// Shared Expert Activations", Eq. 80 and Section 21.3's fixed-router gradients; the
+// SwiGLU expert of "Section 20: One Shared Expert Is All You Need", Eq. 74).
+//
+// With A = X W_g^T, B = X W_u^T, S = SiLU(A), H = S * B and F = H W_d^T per expert, and
+// the upstream gradient dF of each kept route's row equal to r dy (s dy for the shared
+// branch), the chain rule gives
+//   dH = dF W_d,  dA = dH * B * SiLU'(A),  dB = dH * S,  dX = [dA dB] [W_g; W_u],
+//   dW_d = dF^T H,  dW_g = dA^T X,  dW_u = dB^T X.
+// The data-gradient contractions (dH, dX) and the recomputation of A and B run on the
+// forward's persistent grouped GEMM over weights packed in MFMA-operand order (the
+// transposed weights come from transpose_pack_kernel). This file holds the rest:
+//   transpose_pack_kernel  packs W^T (optionally two matrices stacked along the
+//                          contraction) in the MFMA-operand order, through an LDS tile
+//   grad_rows_kernel       dF rows (r dy gathered into the packed expert order) and the
+//                          shared branch's s dy, one wave per token
+//   swiglu_bwd_kernel      dA | dB and H from dH, A, B (fp32 math, bf16 out)
+//   wgrad_kernel           weight gradients, a grouped GEMM contracting over each
+//                          expert's ragged row segment: 64-row stages of both operands are
+//                          loaded 8 x 8 per thread, transposed in registers and stored to
+//                          LDS k-contiguous, so each MFMA operand is one 16-byte LDS read;
+//                          the next stage's global loads are in flight during the MFMAs.
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+// ---- transpose into the packed operand order ----------------------------------------
+// dst[g][nb][kb][lane][8] = Wt[g][32 nb + (lane & 31)][16 kb + 8 (lane >> 5) + 0..7], with
+// Wt[g][n][k] = S[g][k][n] and S = [A; B] stacked along k (A has Ka rows, B the rest).
+constexpr int TP = 64;        // tile edge (k and n)
+constexpr int TP_LD = TP + 8; // padded LDS row (n)
+
+__global__ void __launch_bounds__(256)
+transpose_pack_kernel(int Nn, int Kk, int Ka, const uint16_t* __restrict__ A,
+                      const uint16_t* __restrict__ B, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[TP][TP_LD];
+  const int kt = Kk / TP, nt = Nn / TP;
+  const int bid = blockIdx.x;
+  const int n_tile = bid % nt;
+  const int k_tile = (bid / nt) % kt;
+  const long g = bid / (nt * kt);
+  const int k0 = k_tile * TP, n0 = n_tile * TP;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // 64 rows x 8 pieces of 16 bytes
+    const int piece = tid + h * 256;
+    const int kr = piece >> 3, c = (piece & 7) * 8;
+    const int k = k0 + kr;
+    const uint16_t* src = k < Ka ? A + (g * Ka + k) * static_cast<long>(Nn)
+                                 : B + (g * (Kk - Ka) + (k - Ka)) * static_cast<long>(Nn);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + n0 + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[kr][c + 2 * i] = static_cast<uint16_t>(v[i] & 0xFFFFu);
+      tile[kr][c + 2 * i + 1] = static_cast<uint16_t>(v[i] >> 16);
+    }
+  }
+  __syncthreads();
+  const int KB = Kk / 16, NB = Nn / 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // 2 n-blocks x 4 k-blocks x 64 lanes
+    const int piece = tid + h * 256;
+    const int lane = piece & 63, blk = piece >> 6;
+    const int nbl = blk >> 2, kbl = blk & 3;
+    const int nl = 32 * nbl + (lane & 31), kl = 16 * kbl + 8 * (lane >> 5);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = static_cast<uint32_t>(tile[kl + 2 * i][nl]) |
+             (static_cast<uint32_t>(tile[kl + 2 * i + 1][nl]) << 16);
+    const long nb = n0 / 32 + nbl, kb = k0 / 16 + kbl;
+    reinterpret_cast<u32x4*>(dst)[((g * NB + nb) * KB + kb) * 64 + lane] = o;
+  }
+}
+
+// ---- upstream gradient rows ---------------------------------------------------------
+constexpr int GR_WAVES = 4;
+
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 u, float c) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(u[i] << 16) * c;
+    const float hi = __uint_as_float(u[i] & 0xFFFF0000u) * c;
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return o;
+}
+
+// dF[dest_row[t][k]] = r[t][k] dy[t] for kept routes; dG[t] = s_t dy[t] when dG != null
+__global__ void __launch_bounds__(GR_WAVES * kWave)
+grad_rows_kernel(int T, int d, int K, const uint16_t* __restrict__ dy,
+                 const int32_t* __restrict__ dest_row, const float* __restrict__ topk_r,
+                 float s, const float* __restrict__ s_tok, uint16_t* __restrict__ dF,
+                 uint16_t* __restrict__ dG) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * GR_WAVES + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int dk = -1;
+  float rk = 0.f;
+  if (lane < K) {
+    dk = dest_row[static_cast<size_t>(t) * K + lane];
+    rk = topk_r[static_cast<size_t>(t) * K + lane];
+  }
+  const float st = s_tok != nullptr ? s_tok[t] : s;
+  const int npc = d / 8;
+  for (int j = lane; j < npc; j += kWave) {
+    const u32x4 u = reinterpret_cast<const u32x4*>(dy + static_cast<size_t>(t) * d)[j];
+    for (int k = 0; k < K; ++k) {
+      const int row = __shfl(dk, k, kWave);
+      const float rr = __shfl(rk, k, kWave);
+      if (row < 0) continue;
+      reinterpret_cast<u32x4*>(dF + static_cast<size_t>(row) * d)[j] = scale_bf16x8(u, rr);
+    }
+    if (dG != nullptr)
+      reinterpret_cast<u32x4*>(dG + static_cast<size_t>(t) * d)[j] = scale_bf16x8(u, st);
+  }
+}
+
+// ---- SwiGLU backward ----------------------------------------------------------------
+// rows [0, rows_dev ? *rows_dev : rows): dAB[j] = [dA | dB] (2 d_ff wide), H[j] = S * B
+__global__ void __launch_bounds__(256)
+swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
+                  const uint16_t* __restrict__ dH, const uint16_t* __restrict__ Av,
+                  const uint16_t* __restrict__ Bv, uint16_t* __restrict__ dAB,
+                  uint16_t* __restrict__ H) {
+  const int R = rows_dev != nullptr ? min(rows, *rows_dev) : rows;
+  const int per_row = dff / 8;
+  const long total = static_cast<long>(R) * per_row;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += static_cast<long>(gridDim.x) * 256) {
+    const long j = i / per_row;
+    const int c = static_cast<int>(i % per_row) * 8;
+    const size_t o = static_cast<size_t>(j) * dff + c;
+    const u32x4 uh = *reinterpret_cast<const u32x4*>(dH + o);
+    const u32x4 ua = *reinterpret_cast<const u32x4*>(Av + o);
+    const u32x4 ub = *reinterpret_cast<const u32x4*>(Bv + o);
+    u32x4 oa, ob, oh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float da[2], db[2], hh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float g = __uint_as_float(h ? (uh[q] & 0xFFFF0000u) : (uh[q] << 16));
+        const float a = __uint_as_float(h ? (ua[q] & 0xFFFF0000u) : (ua[q] << 16));
+        const float b = __uint_as_float(h ? (ub[q] & 0xFFFF0000u) : (ub[q] << 16));
+        const float sg = 1.0f / (1.0f + expf(-a));
+        const float sa = a * sg;
+        db[h] = g * sa;
+        da[h] = g * b * sg * (1.0f + a * (1.0f - sg));
+        hh[h] = sa * b;
+      }
+      oa[q] = pack_bf16x2(da[0], da[1]);
+      ob[q] = pack_bf16x2(db[0], db[1]);
+      oh[q] = pack_bf16x2(hh[0], hh[1]);
+    }
+    const size_t o2 = static_cast<size_t>(j) * 2 * dff + c;
+    *reinterpret_cast<u32x4*>(dAB + o2) = oa;
+    *reinterpret_cast<u32x4*>(dAB + o2 + dff) = ob;
+    *reinterpret_cast<u32x4*>(H + o) = oh;
+  }
+}
+
+// ---- weight gradients: out[g][m][n] = sum_{j in segment g} P[j][m] Q[row(j)][n] ---------
+constexpr int WG_BM = 128, WG_BN = 128, WG_BK = 64;
+constexpr int WG_LD = WG_BK + 8;  // padded LDS row (k), 144 bytes
+
+struct WgradProblem {
+  const uint16_t* P;      // [rows][ldp], columns [0, M) used
+  int ldp;
+  const uint16_t* Q;      // [*][ldq], row j or row_index[j]; columns [0, Nc)
+  int ldq;
+  const int32_t* row_index;
+  const int32_t* offsets; // [G+1] device, or null: one segment [0, rows)
+  int rows;
+  int G, M, Nc;
+  float* out;             // [G][M][Nc]
+};
+
+// 8 rows x 8 columns of bf16 -> 8 columns x 8 rows (k-contiguous per column)
+__device__ __forceinline__ void transpose8(const u32x4 (&v)[8], u32x4 (&o)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = v[2 * p][q], b = v[2 * p + 1][q];
+      o[2 * q][p] = (a & 0xFFFFu) | (b << 16);
+      o[2 * q + 1][p] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+wgrad_kernel(WgradProblem pb, int tiles_m, int tiles_n, int total) {
+  // one LDS stage (37 KB: four workgroups per CU); the next stage's global loads are in
+  // registers while the MFMAs read the current one
+  __shared__ __attribute__((aligned(16))) uint16_t sP[WG_BM * WG_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[WG_BN * WG_LD];
+  // consecutive workgroups land on different XCDs: give each XCD a contiguous range of
+  // tiles so that the tiles of one expert share an L2
+  const int b = blockIdx.x;
+  const int per_xcd = (total + 7) / 8;
+  const int tile = (b % 8) * per_xcd + b / 8;
+  if (tile >= total) return;
+  const int tn = tile % tiles_n;
+  const int tm = (tile / tiles_n) % tiles_m;
+  const int g = tile / (tiles_n * tiles_m);
+  const int m0 = tm * WG_BM, n0 = tn * WG_BN;
+  const int j0 = pb.offsets != nullptr ? pb.offsets[g] : 0;
+  const int j1 = pb.offsets != nullptr ? pb.offsets[g + 1] : pb.rows;
+  const int nst = (j1 - j0 + WG_BK - 1) / WG_BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  // loader role: waves 0-1 load P, waves 2-3 load Q; each wave covers the stage's 64
+  // rows x 64 columns, a lane an 8 (k) x 8 (column) block. Consecutive lanes take
+  // consecutive row blocks: with 144-byte LDS rows, each group of 8 lanes of a 16-byte
+  // LDS store then covers 32 distinct banks.
+  const bool isP = w < 2;
+  const int kb = lane & 7, cb = (w & 1) * 8 + (lane >> 3);
+  const int col = (isP ? m0 : n0) + cb * 8;
+  const bool col_ok = col < (isP ? pb.M : pb.Nc);
+  const uint16_t* base = (isP ? pb.P : pb.Q) + (col_ok ? col : 0);
+  const int ld = isP ? pb.ldp : pb.ldq;
+  const int32_t* gather = isP ? nullptr : pb.row_index;
+
+  // every row index first, then every row: two round trips per stage at most
+  auto load = [&](int s, u32x4 (&v)[8], uint32_t& okm) {
+    long row[8];
+    okm = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int j = j0 + s * WG_BK + kb * 8 + r;
+      const bool ok = col_ok && j < j1;
+      okm |= ok ? (1u << r) : 0u;
+      row[r] = ok ? j : j0;  // a valid row: j0 < j1 whenever a stage exists
+    }
+    if (gather != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) row[r] = gather[row[r]];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const u32x4*>(base + row[r] * ld);
+  };
+  auto store = [&](const u32x4 (&v)[8], uint32_t okm) {
+    u32x4 z[8], o[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) z[r] = ((okm >> r) & 1u) ? v[r] : u32x4{0u, 0u, 0u, 0u};
+    transpose8(z, o);
+    uint16_t* dst = isP ? sP : sQ;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<u32x4*>(dst + (cb * 8 + c) * WG_LD + kb * 8) = o[c];
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+
+  u32x4 v[8];
+  uint32_t okm = 0;
+  if (nst > 0) {
+    load(0, v, okm);
+    store(v, okm);
+  }
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) load(s + 1, v, okm);  // in flight during the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < WG_BK / 16; ++kk) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = wm * 64 + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(sP + m * WG_LD + kk * 16 + (lane >> 5) * 8);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int n = wn * 64 + jj * 32 + (lane & 31);
+        bf[jj] = *reinterpret_cast<const bf16x8*>(sQ + n * WG_LD + kk * 16 + (lane >> 5) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+    }
+    if (s + 1 < nst) {
+      __syncthreads();  // every wave is done reading this stage
+      store(v, okm);
+      __syncthreads();
+    }
+  }
+  // lane holds rows m = 8 (v / 4) + 4 (lane / 32) + v % 4 and column n = lane % 32
+  float* out = pb.out + static_cast<size_t>(g) * pb.M * pb.Nc;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
+      if (n >= pb.Nc) continue;
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+        if (m < pb.M) out[static_cast<size_t>(m) * pb.Nc + n] = acc[i][jj][vv];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_pack(int G, int Nn, int Kk, int Ka, const void* A, const void* B,
+                                 void* dst, hipStream_t stream) {
+  const long grid = static_cast<long>(G) * (Kk / TP) * (Nn / TP);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_pack_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     stream, Nn, Kk, Ka, static_cast<const uint16_t*>(A),
+                     static_cast<const uint16_t*>(B), static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_rows(int T, int d, int K, const void* dy, const int32_t* dest_row,
+                            const float* topk_r, float s, const float* s_tok, void* dF,
+                            void* dG, hipStream_t stream) {
+  const int grid = (T + GR_WAVES - 1) / GR_WAVES;
+  hipLaunchKernelGGL(grad_rows_kernel, dim3(grid), dim3(GR_WAVES * kWave), 0, stream, T, d, K,
+                     static_cast<const uint16_t*>(dy), dest_row, topk_r, s, s_tok,
+                     static_cast<uint16_t*>(dF), static_cast<uint16_t*>(dG));
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(int rows, const int32_t* rows_dev, int dff, const void* dH,
+                             const void* A, const void* B, void* dAB, void* H,
+                             hipStream_t stream) {
+  const long total = static_cast<long>(rows) * (dff / 8);
+  if (total <= 0) return hipSuccess;
+  long grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     rows, rows_dev, dff, static_cast<const uint16_t*>(dH),
+                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B),
+                     static_cast<uint16_t*>(dAB), static_cast<uint16_t*>(H));
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(int G, int M, int Nc, const void* P, int ldp, const void* Q, int ldq,
+                        const int32_t* row_index, const int32_t* offsets, int rows, float* out,
+                        hipStream_t stream) {
+  WgradProblem pb{static_cast<const uint16_t*>(P), ldp, static_cast<const uint16_t*>(Q), ldq,
+                  row_index, offsets, rows, G, M, Nc, out};
+  const int tiles_m = (M + WG_BM - 1) / WG_BM, tiles_n = (Nc + WG_BN - 1) / WG_BN;
+  const long total = static_cast<long>(G) * tiles_m * tiles_n;
+  if (total <= 0) return hipSuccess;
+  if (total > 0x3fffffffL) return hipErrorInvalidValue;
+  const long grid = (total + 7) / 8 * 8;
+  hipLaunchKernelGGL(wgrad_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, pb,
+                     tiles_m, tiles_n, static_cast<int>(total));
+  return hipGetLastError();
+}

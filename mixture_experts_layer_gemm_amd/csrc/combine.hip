@@ -37,7 +37,7 @@ combine_kernel(int T, int d, int K, const void* __restrict__ f_perm,
   float rk = 0.f;
   if (lane < K) {
     dk = dest_row[static_cast<size_t>(t) * K + lane];
-    rk = topk_r[static_cast<size_t>(t) * K + lane];
+    rk = topk_r != nullptr ? topk_r[static_cast<size_t>(t) * K + lane] : 1.0f;
   }
   const float st = (s_tok != nullptr) ? s_tok[t] : s;
   const int npc = d / EPP;

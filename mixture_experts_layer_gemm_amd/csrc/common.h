@@ -101,6 +101,20 @@ hipError_t launch_grouped_gemm_packed(bool swiglu, int G, int K_dim, int N_dim, 
 hipError_t launch_pack_weights(int G, int N_dim, int K_dim, const void* w, void* w_packed,
                                hipStream_t stream);
 
+// backward (router held fixed)
+hipError_t launch_transpose_pack(int G, int Nn, int Kk, int Ka, const void* A, const void* B,
+                                 void* dst, hipStream_t stream);
+hipError_t launch_grad_rows(int T, int d, int K, const void* dy, const int32_t* dest_row,
+                            const float* topk_r, float s, const float* s_tok, void* dF,
+                            void* dG, hipStream_t stream);
+hipError_t launch_swiglu_bwd(int rows, const int32_t* rows_dev, int dff, const void* dH,
+                             const void* A, const void* B, void* dAB, void* H,
+                             hipStream_t stream);
+hipError_t launch_wgrad(int G, int M, int Nc, const void* P, int ldp, const void* Q, int ldq,
+                        const int32_t* row_index, const int32_t* offsets, int rows, float* out,
+                        hipStream_t stream);
+
+// topk_r == nullptr: unit coefficients
 hipError_t launch_combine(int T, int d_model, int K, int dt, const void* f_perm,
                           const int32_t* dest_row, const float* topk_r, const void* g,
                           float s, const float* s_tok, void* y, hipStream_t stream);

@@ -15,7 +15,7 @@
 // affinities divided by their sum) with butterfly reductions and adds them to per-lane
 // column sums; lanes k < K accumulate the dropped slots and their coefficients. The four
 // waves' partials are added in a fixed order and written per workgroup.
-// stats_final_kernel: 1024 threads add the partials column by column (threads split the
+// stats_final_kernel: 256 threads add the partials column by column (threads split the
 // workgroups of each expert, eight independent loads in flight, then a fixed-order sum in
 // fp64); wave 0 then derives every statistic with fp64 butterfly reductions over the
 // experts. No atomics: results are bitwise repeatable.
@@ -156,7 +156,7 @@ stats_partial_kernel(int T, int N, int K, int score, int tpb, const float* __res
   }
 }
 
-constexpr int SF_THREADS = 1024;
+constexpr int SF_THREADS = 256;
 
 __global__ void __launch_bounds__(SF_THREADS)
 stats_final_kernel(int T, int N, int K, int group, int nblk, int NP,
@@ -253,11 +253,12 @@ stats_final_kernel(int T, int N, int K, int group, int nblk, int NP,
   }
   mrreq = st_wave_max_d(mrreq);
   mrkeep = st_wave_max_d(mrkeep);
-  double d[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    d[v] = 0.0;
-    for (int q = 0; q < 16; ++q) d[v] += dpart[q * 4 + v];  // fixed order
+  double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+  for (int q = 0; q < 16; ++q) {  // fixed order
+    d0 += dpart[q * 4];
+    d1 += dpart[q * 4 + 1];
+    d2 += dpart[q * 4 + 2];
+    d3 += dpart[q * 4 + 3];
   }
   if (lane == 0) {
     const double nan = __builtin_nan("");
@@ -272,9 +273,9 @@ stats_final_kernel(int T, int N, int K, int group, int nblk, int NP,
     stats[MOE_STAT_CV_KEEP] = static_cast<float>(mean_keep > 0 ? sqrt(vkeep) / mean_keep : nan);
     stats[MOE_STAT_NEVER_SELECTED] = static_cast<float>(never);
     stats[MOE_STAT_DELTA_ROUTE] = static_cast<float>((KT - skeep) / KT);
-    stats[MOE_STAT_TOKENS_LOST_ANY] = static_cast<float>(d[0]);
-    stats[MOE_STAT_TOKENS_LOST_ALL] = static_cast<float>(d[1]);
-    stats[MOE_STAT_WEIGHT_REMOVED] = static_cast<float>(d[3] > 0 ? d[2] / d[3] : nan);
+    stats[MOE_STAT_TOKENS_LOST_ANY] = static_cast<float>(d0);
+    stats[MOE_STAT_TOKENS_LOST_ALL] = static_cast<float>(d1);
+    stats[MOE_STAT_WEIGHT_REMOVED] = static_cast<float>(d3 > 0 ? d2 / d3 : nan);
     // destination totals sum to the expert totals
     stats[MOE_STAT_IMAX_RANK_REQ] = static_cast<float>(M > 0 && sreq > 0 ? M * mrreq / sreq : nan);
     stats[MOE_STAT_IMAX_RANK_KEEP] = static_cast<float>(M > 0 && skeep > 0 ? M * mrkeep / skeep : nan);

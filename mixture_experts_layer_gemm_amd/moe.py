@@ -42,6 +42,16 @@ class ForwardArgs(ctypes.Structure):
                                 "row_token", "x_perm", "h_perm", "f_perm", "g", "balance_P",
                                 "balance_stats", "count_accum")]
 
+class BackwardArgs(ctypes.Structure):
+    """Mirror of moe_backward_args (include/moe.h)."""
+    _fields_ = [(n, c_int) for n in ("T", "d_model", "N", "K", "d_r", "d_s", "dt")] + [
+        ("s", c_float), ("max_rows", c_int)] + [
+        (n, c_void_p) for n in ("x", "dy", "row_token", "offsets", "dest_row", "topk_r", "s_tok",
+                                "w_gate", "w_up", "wt_down", "wt_gate_up", "ws_gate", "ws_up",
+                                "wst_down", "wst_gate_up", "dx", "dw_gate", "dw_up", "dw_down",
+                                "dws_gate", "dws_up", "dws_down")]
+
+
 # order of moe_balance_stats' output vector (enum moe_stat)
 STAT_NAMES = ["lbl", "imax_req", "imax_keep", "ih_req", "ih_keep", "cv_req", "cv_keep",
               "never_selected", "delta_route", "tokens_lost_any", "tokens_lost_all",
@@ -62,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "moe_route_workspace_size": (S, [I, I, I]),
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_bias_update": (I, [I, F, P, P, I, P]),
+        "moe_pack_weights_transposed": (I, [I, I, I, I, I, P, P, P, P]),
+        "moe_backward_workspace_size": (S, [P]),
+        "moe_backward": (I, [P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
         "moe_grouped_swiglu": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P]),
@@ -308,6 +321,62 @@ def moe_combine(f_perm, dest_row, topk_r, g=None, s: float = 1.0, s_tok=None, y=
     return y
 
 
+def moe_pack_weights_transposed(w_a, w_b=None):
+    """[G][Ka][N] (stacked over [G][Kb][N] when w_b is given) bf16 -> the packed transpose
+    [G][N][Ka + Kb], the operand of the backward's data-gradient contractions."""
+    G, Ka, Nn = w_a.shape
+    Kk = Ka + (0 if w_b is None else w_b.shape[1])
+    dst = torch.empty(G, Nn, Kk, dtype=w_a.dtype, device=w_a.device)
+    st = lib.moe_pack_weights_transposed(G, Nn, Kk, Ka, _dt(w_a), _ptr(w_a.contiguous()),
+                                         _ptr(None if w_b is None else w_b.contiguous()),
+                                         _ptr(dst), _stream())
+    _check("moe_pack_weights_transposed", st)
+    return dst
+
+
+def backward_weights(w_gate, w_up, w_down):
+    """Packed transposes used by moe_backward: w_down^T [N][d_r][d] and [w_gate; w_up]^T
+    [N][d][2 d_r] (row-major bf16 inputs, as in a Linear layer)."""
+    return moe_pack_weights_transposed(w_down), moe_pack_weights_transposed(w_gate, w_up)
+
+
+def moe_backward(x, dy, routing: dict, max_rows: int, w_gate, w_up, wt_down, wt_gate_up,
+                 shared=None, s: float = 1.0):
+    """Fixed-router gradients of the layer for upstream dy. `routing` holds the forward's
+    row_token, offsets, dest_row, topk_r (and s_tok when the shared gate is learned);
+    w_gate/w_up are packed, wt_* the packed transposes (backward_weights); `shared` is
+    (ws_gate, ws_up, wst_down, wst_gate_up) of the one shared MLP (packed), or None.
+    Returns dict(dx, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down)."""
+    T, d = x.shape
+    N, d_r, _ = w_gate.shape
+    K = routing["dest_row"].shape[1]
+    dev = x.device
+    d_s = 0 if shared is None else shared[0].shape[0]
+    f32 = torch.float32
+    out = dict(dx=torch.empty_like(x), dw_gate=torch.empty(N, d_r, d, dtype=f32, device=dev),
+               dw_up=torch.empty(N, d_r, d, dtype=f32, device=dev),
+               dw_down=torch.empty(N, d, d_r, dtype=f32, device=dev),
+               dws_gate=torch.empty(d_s, d, dtype=f32, device=dev) if d_s else None,
+               dws_up=torch.empty(d_s, d, dtype=f32, device=dev) if d_s else None,
+               dws_down=torch.empty(d, d_s, dtype=f32, device=dev) if d_s else None)
+    a = BackwardArgs()
+    a.T, a.d_model, a.N, a.K, a.d_r, a.d_s, a.dt = T, d, N, K, d_r, d_s, _dt(x)
+    a.s, a.max_rows = float(s), int(max_rows)
+    a.x, a.dy = _ptr(x), _ptr(dy)
+    for name in ("row_token", "offsets", "dest_row", "topk_r", "s_tok"):
+        setattr(a, name, _ptr(routing.get(name)))
+    a.w_gate, a.w_up, a.wt_down, a.wt_gate_up = (_ptr(w) for w in (w_gate, w_up, wt_down, wt_gate_up))
+    if shared is not None:
+        a.ws_gate, a.ws_up, a.wst_down, a.wst_gate_up = (_ptr(w) for w in shared)
+    for name in ("dx", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down"):
+        setattr(a, name, _ptr(out[name]))
+    ws = _workspace(lib.moe_backward_workspace_size(ctypes.byref(a)), dev)
+    st = lib.moe_backward(ctypes.byref(a), _ptr(ws), ws.numel(), _stream())
+    _check("moe_backward", st)
+    out["_workspace"] = ws          # kept alive until the caller synchronizes
+    return out
+
+
 def pack_shared(shared: Sequence) -> tuple:
     """Several ungated shared experts -> one MLP: gate/up rows concatenated, down columns
     concatenated (Section 20, Eq. 75). A weight-layout step, done once at load time."""
@@ -328,7 +397,7 @@ class MoELayer:
                  renorm: bool = True, alpha: float = 1.0, s: float = 1.0, capacity: int = -1,
                  capacity_group: int = 0, logit_bias=None, w_shared_gate=None, shared=None, keep_intermediates=False,
                  pack_weights=None, keep_x_perm=False, balance_stats=False, expert_bias=None,
-                 count_accum=None):
+                 count_accum=None, trainable=False):
         self.x = x
         T, d = x.shape
         N, d_r, _ = w_gate.shape
@@ -337,6 +406,17 @@ class MoELayer:
         if pack_weights is None:                      # the fast path whenever it applies
             pack_weights = x.dtype == torch.bfloat16
         self.weights_packed = bool(pack_weights)
+        self.bwd = None
+        if trainable:           # fixed-router backward: packed transposes, routing kept
+            if x.dtype != torch.bfloat16:
+                raise MoEError("moe_backward", MOE_ERR_UNSUPPORTED)
+            pack_weights, keep_intermediates = True, True
+            bwd = dict(zip(("wt_down", "wt_gate_up"), backward_weights(w_gate, w_up, w_down)))
+            if shared_mlp:
+                sg, su, sd = shared_mlp
+                bwd["shared_t"] = (moe_pack_weights_transposed(sd[None])[0],
+                                   moe_pack_weights_transposed(sg[None], su[None])[0])
+            self.bwd = bwd
         if self.weights_packed:
             w_gate, w_up, w_down = (moe_pack_weights(w) for w in (w_gate, w_up, w_down))
             if shared_mlp:
@@ -391,6 +471,18 @@ class MoELayer:
                              _stream() if stream is None else stream)
         _check("moe_forward", st)
         return self.y
+
+    def backward(self, dy):
+        """Fixed-router gradients for the last forward (needs trainable=True)."""
+        if self.bwd is None:
+            raise MoEError("moe_backward", MOE_ERR_INVALID_ARG)
+        t = self.tensors
+        shared = None
+        if self.shared_mlp:
+            shared = (self.shared_mlp[0], self.shared_mlp[1]) + self.bwd["shared_t"]
+        return moe_backward(self.x, dy, self.out, self.rows, t["w_gate"], t["w_up"],
+                            self.bwd["wt_down"], self.bwd["wt_gate_up"], shared=shared,
+                            s=self.args.s)
 
 
 def moe_forward(x, w_router, w_gate, w_up, w_down, K: int, **kw):
