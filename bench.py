@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP graph replays of the forward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -164,14 +166,34 @@ def main():
     for _ in range(args.warmup):
         layer.forward()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        layer.forward()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+
+    def timed(step):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # eager: every step enqueues the forward's kernels one by one
+    ms_eager = timed(layer.forward)
+    ms = ms_eager
+    if not args.eager:
+        # the same forward captured once in a HIP graph; each step is one replay
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            layer.forward()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.forward()
+        for _ in range(args.warmup):
+            graph.replay()
+        ms = timed(graph.replay)
     tokens_per_s = T / (ms / 1e3)
 
     # ---- per-stage timing on the layer's own buffers ------------------------------
@@ -274,6 +296,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "launch": "eager" if args.eager else "hip_graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
