@@ -609,18 +609,14 @@ int moe_backward(const moe_backward_args* a, void* workspace, size_t workspace_b
   MOE_HIP(launch_combine(T, d, K, MOE_BF16, w.dXp, a->dest_row, nullptr, sh ? w.dXs : nullptr,
                          1.0f, nullptr, a->dx, stream));
   // weight gradients, contracting over each expert's rows (zero for experts without rows)
-  MOE_HIP(launch_wgrad(N, d, dr, w.dF, d, w.H, dr, nullptr, a->offsets, R, a->dw_down, stream));
+  // (the shared MLP's gradients ride in the same launches: a dense second problem)
+  MOE_HIP(launch_wgrad(N, d, dr, w.dF, d, w.H, dr, nullptr, a->offsets, R, a->dw_down,
+                       d, ds, w.dG, d, w.Hs, ds, T, sh ? a->dws_down : nullptr, stream));
   MOE_HIP(launch_wgrad(N, dr, d, w.dAB, 2 * dr, a->x, d, a->row_token, a->offsets, R, a->dw_gate,
-                       stream));
+                       ds, d, w.dABs, 2 * ds, a->x, d, T, sh ? a->dws_gate : nullptr, stream));
   MOE_HIP(launch_wgrad(N, dr, d, w.dAB + dr, 2 * dr, a->x, d, a->row_token, a->offsets, R,
-                       a->dw_up, stream));
-  if (sh) {
-    MOE_HIP(launch_wgrad(1, d, ds, w.dG, d, w.Hs, ds, nullptr, nullptr, T, a->dws_down, stream));
-    MOE_HIP(launch_wgrad(1, ds, d, w.dABs, 2 * ds, a->x, d, nullptr, nullptr, T, a->dws_gate,
-                         stream));
-    MOE_HIP(launch_wgrad(1, ds, d, w.dABs + ds, 2 * ds, a->x, d, nullptr, nullptr, T, a->dws_up,
-                         stream));
-  }
+                       a->dw_up, ds, d, sh ? w.dABs + ds : nullptr, 2 * ds, a->x, d, T,
+                       sh ? a->dws_up : nullptr, stream));
   return MOE_OK;
 }
 

@@ -191,17 +191,36 @@ __device__ __forceinline__ void transpose8(const u32x4 (&v)[8], u32x4 (&o)[8]) {
 }
 
 __global__ void __launch_bounds__(256)
-wgrad_kernel(WgradProblem pb, int tiles_m, int tiles_n, int total) {
+wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   // one LDS stage (37 KB: four workgroups per CU); the next stage's global loads are in
   // registers while the MFMAs read the current one
   __shared__ __attribute__((aligned(16))) uint16_t sP[WG_BM * WG_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sQ[WG_BN * WG_LD];
   // consecutive workgroups land on different XCDs: give each XCD a contiguous range of
-  // tiles so that the tiles of one expert share an L2
+  // tiles so that the tiles of one expert share an L2. The second problem (the shared
+  // MLP: few tiles, each contracting over every token) comes first in every XCD's range,
+  // so its long tiles start first and the short expert tiles fill in around them.
   const int b = blockIdx.x;
-  const int per_xcd = (total + 7) / 8;
-  const int tile = (b % 8) * per_xcd + b / 8;
-  if (tile >= total) return;
+  const int xcd = b % 8, local = b / 8;
+  const bool second = local < s_per;
+  const int tile = second ? xcd * s_per + local : xcd * r_per + (local - s_per);
+  // the tile's problem, field by field (a reference to either argument would be copied
+  // to scratch)
+  WgradProblem pb;
+  pb.P = second ? q1.P : q0.P;
+  pb.ldp = second ? q1.ldp : q0.ldp;
+  pb.Q = second ? q1.Q : q0.Q;
+  pb.ldq = second ? q1.ldq : q0.ldq;
+  pb.row_index = second ? q1.row_index : q0.row_index;
+  pb.offsets = second ? q1.offsets : q0.offsets;
+  pb.rows = second ? q1.rows : q0.rows;
+  pb.G = second ? q1.G : q0.G;
+  pb.M = second ? q1.M : q0.M;
+  pb.Nc = second ? q1.Nc : q0.Nc;
+  pb.out = second ? q1.out : q0.out;
+  const int tiles_m = (pb.M + WG_BM - 1) / WG_BM, tiles_n = (pb.Nc + WG_BN - 1) / WG_BN;
+  const int total = pb.G * tiles_m * tiles_n;
+  if ((second ? local : local - s_per) >= (second ? s_per : r_per) || tile >= total) return;
   const int tn = tile % tiles_n;
   const int tm = (tile / tiles_n) % tiles_m;
   const int g = tile / (tiles_n * tiles_m);
@@ -351,15 +370,21 @@ hipError_t launch_swiglu_bwd(int rows, const int32_t* rows_dev, int dff, const v
 
 hipError_t launch_wgrad(int G, int M, int Nc, const void* P, int ldp, const void* Q, int ldq,
                         const int32_t* row_index, const int32_t* offsets, int rows, float* out,
-                        hipStream_t stream) {
-  WgradProblem pb{static_cast<const uint16_t*>(P), ldp, static_cast<const uint16_t*>(Q), ldq,
+                        int M1, int Nc1, const void* P1, int ldp1, const void* Q1, int ldq1,
+                        int rows1, float* out1, hipStream_t stream) {
+  WgradProblem q0{static_cast<const uint16_t*>(P), ldp, static_cast<const uint16_t*>(Q), ldq,
                   row_index, offsets, rows, G, M, Nc, out};
-  const int tiles_m = (M + WG_BM - 1) / WG_BM, tiles_n = (Nc + WG_BN - 1) / WG_BN;
-  const long total = static_cast<long>(G) * tiles_m * tiles_n;
-  if (total <= 0) return hipSuccess;
-  if (total > 0x3fffffffL) return hipErrorInvalidValue;
-  const long grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL(wgrad_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, pb,
-                     tiles_m, tiles_n, static_cast<int>(total));
+  WgradProblem q1{static_cast<const uint16_t*>(P1), ldp1, static_cast<const uint16_t*>(Q1), ldq1,
+                  nullptr, nullptr, rows1, out1 != nullptr ? 1 : 0, M1, Nc1, out1};
+  auto tiles = [](const WgradProblem& q) -> long {
+    return static_cast<long>(q.G) * ((q.M + WG_BM - 1) / WG_BM) * ((q.Nc + WG_BN - 1) / WG_BN);
+  };
+  const long t0 = tiles(q0), t1 = out1 != nullptr ? tiles(q1) : 0;
+  if (t0 + t1 <= 0) return hipSuccess;
+  if (t0 + t1 > 0x3fffffffL) return hipErrorInvalidValue;
+  const long s_per = (t1 + 7) / 8, r_per = (t0 + 7) / 8;
+  const long grid = 8 * (s_per + r_per);
+  hipLaunchKernelGGL(wgrad_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, q0,
+                     q1, static_cast<int>(s_per), static_cast<int>(r_per));
   return hipGetLastError();
 }

@@ -110,9 +110,12 @@ hipError_t launch_grad_rows(int T, int d, int K, const void* dy, const int32_t* 
 hipError_t launch_swiglu_bwd(int rows, const int32_t* rows_dev, int dff, const void* dH,
                              const void* A, const void* B, void* dAB, void* H,
                              hipStream_t stream);
+// weight gradients of G grouped segments (offsets) and, when out1 != nullptr, of one dense
+// problem over rows1 rows (the shared MLP) in the same launch
 hipError_t launch_wgrad(int G, int M, int Nc, const void* P, int ldp, const void* Q, int ldq,
                         const int32_t* row_index, const int32_t* offsets, int rows, float* out,
-                        hipStream_t stream);
+                        int M1, int Nc1, const void* P1, int ldp1, const void* Q1, int ldq1,
+                        int rows1, float* out1, hipStream_t stream);
 
 // topk_r == nullptr: unit coefficients
 hipError_t launch_combine(int T, int d_model, int K, int dt, const void* f_perm,
