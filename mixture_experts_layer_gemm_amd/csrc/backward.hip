@@ -16,11 +16,10 @@
 //                          shared branch's s dy, one wave per token
 //   swiglu_bwd_kernel      dA | dB and H from dH, A, B (fp32 math, bf16 out)
 //   wgrad_kernel           weight gradients, a grouped GEMM contracting over each
-//                          expert's ragged row segment: 64-row stages of both operands are
-//                          loaded 8 x 8 per thread, transposed in registers and stored to
-//                          LDS k-contiguous, so each MFMA operand is one 16-byte LDS read;
-//                          the next stage's global loads are in flight during the MFMAs.
-#include "common.h"
+//                          expert's ragged row segment: rows reach LDS by direct-to-LDS
+//                          loads in a 4-stage ring and the MFMA fragments come out with the
+//                          LDS transpose read (ds_read_b64_tr_b16).
+#include "gemm_common.h"
 
 using namespace moe;
 
@@ -163,8 +162,23 @@ swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
 }
 
 // ---- weight gradients: out[g][m][n] = sum_{j in segment g} P[j][m] Q[row(j)][n] ---------
-constexpr int WG_BM = 128, WG_BN = 128, WG_BK = 64;
-constexpr int WG_LD = WG_BK + 8;  // padded LDS row (k), 144 bytes
+// Both operands are k-major (k = the row j of a segment), while v_mfma_f32_32x32x16_bf16
+// wants 8 consecutive k of one column per lane. The rows go to LDS as they are, by
+// direct-to-LDS loads into a 4-stage ring (32 rows per stage), and the fragments come out
+// with ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i & 3 of the
+// 8-byte pieces that lanes (i >> 2), 4 + (i >> 2), 8 + (i >> 2), 12 + (i >> 2) of the
+// group point at; pointing lane s at column block 4 (s & 3) of row s >> 2 therefore hands
+// lane i four consecutive rows of one column. An 8-byte-unit XOR swizzle per row keeps
+// those reads free of bank conflicts.
+constexpr int W2_BM = 128, W2_BN = 128;       // output tile
+constexpr int W2_BK = 32;                     // segment rows per stage
+constexpr int W2_XS = 4;                      // ring depth (stages)
+constexpr int W2_ROWB = 256;                  // LDS bytes per stage row (128 bf16)
+constexpr int W2_OPB = W2_BK * W2_ROWB;       // bytes per operand per stage
+constexpr int W2_STAGE = 2 * W2_OPB;
+constexpr int W2_DPW = W2_STAGE / (1024 * 4); // direct-to-LDS loads per wave per stage
+constexpr int W2_WAIT = (W2_XS - 2) * W2_DPW; // the two later stages may be pending
+static_assert(W2_DPW == 4, "each wave loads 16 rows of one operand per stage");
 
 struct WgradProblem {
   const uint16_t* P;      // [rows][ldp], columns [0, M) used
@@ -178,24 +192,26 @@ struct WgradProblem {
   float* out;             // [G][M][Nc]
 };
 
-// 8 rows x 8 columns of bf16 -> 8 columns x 8 rows (k-contiguous per column)
-__device__ __forceinline__ void transpose8(const u32x4 (&v)[8], u32x4 (&o)[8]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = v[2 * p][q], b = v[2 * p + 1][q];
-      o[2 * q][p] = (a & 0xFFFFu) | (b << 16);
-      o[2 * q + 1][p] = (a >> 16) | (b & 0xFFFF0000u);
-    }
+// physical 16-byte chunk of logical chunk c (0..15) in stage row r
+__device__ __forceinline__ int w2_swz(int r, int c) {
+  const int q = r & 3;
+  return c ^ (2 * q + 8 * (q & 1));
 }
 
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ void w2_dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+typedef short w2_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) w2_v4s w2_lv4s;
+
+__global__ void __launch_bounds__(256, 2)
 wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
-  // one LDS stage (37 KB: four workgroups per CU); the next stage's global loads are in
-  // registers while the MFMAs read the current one
-  __shared__ __attribute__((aligned(16))) uint16_t sP[WG_BM * WG_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[WG_BN * WG_LD];
+  __shared__ __attribute__((aligned(1024))) char ring[W2_XS * W2_STAGE];
+  typedef __attribute__((address_space(3))) char lds_char;
   // consecutive workgroups land on different XCDs: give each XCD a contiguous range of
   // tiles so that the tiles of one expert share an L2. The second problem (the shared
   // MLP: few tiles, each contracting over every token) comes first in every XCD's range,
@@ -218,59 +234,82 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   pb.M = second ? q1.M : q0.M;
   pb.Nc = second ? q1.Nc : q0.Nc;
   pb.out = second ? q1.out : q0.out;
-  const int tiles_m = (pb.M + WG_BM - 1) / WG_BM, tiles_n = (pb.Nc + WG_BN - 1) / WG_BN;
+  const int tiles_m = (pb.M + W2_BM - 1) / W2_BM, tiles_n = (pb.Nc + W2_BN - 1) / W2_BN;
   const int total = pb.G * tiles_m * tiles_n;
   if ((second ? local : local - s_per) >= (second ? s_per : r_per) || tile >= total) return;
   const int tn = tile % tiles_n;
   const int tm = (tile / tiles_n) % tiles_m;
   const int g = tile / (tiles_n * tiles_m);
-  const int m0 = tm * WG_BM, n0 = tn * WG_BN;
-  const int j0 = pb.offsets != nullptr ? pb.offsets[g] : 0;
-  const int j1 = pb.offsets != nullptr ? pb.offsets[g + 1] : pb.rows;
-  const int nst = (j1 - j0 + WG_BK - 1) / WG_BK;
+  const int m0 = tm * W2_BM, n0 = tn * W2_BN;
+  const int j0 = __builtin_amdgcn_readfirstlane(pb.offsets != nullptr ? pb.offsets[g] : 0);
+  const int j1 = __builtin_amdgcn_readfirstlane(pb.offsets != nullptr ? pb.offsets[g + 1] : pb.rows);
+  const int nst = (j1 - j0 + W2_BK - 1) / W2_BK;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  // loader role: waves 0-1 load P, waves 2-3 load Q; each wave covers the stage's 64
-  // rows x 64 columns, a lane an 8 (k) x 8 (column) block. Consecutive lanes take
-  // consecutive row blocks: with 144-byte LDS rows, each group of 8 lanes of a 16-byte
-  // LDS store then covers 32 distinct banks.
-  const bool isP = w < 2;
-  const int kb = lane & 7, cb = (w & 1) * 8 + (lane >> 3);
-  const int col = (isP ? m0 : n0) + cb * 8;
-  const bool col_ok = col < (isP ? pb.M : pb.Nc);
-  const uint16_t* base = (isP ? pb.P : pb.Q) + (col_ok ? col : 0);
-  const int ld = isP ? pb.ldp : pb.ldq;
-  const int32_t* gather = isP ? nullptr : pb.row_index;
+  const uint32_t lds0 = static_cast<uint32_t>((size_t)((lds_char*)ring));
 
-  // every row index first, then every row: two round trips per stage at most
-  auto load = [&](int s, u32x4 (&v)[8], uint32_t& okm) {
-    long row[8];
-    okm = 0;
+  // loads: waves 0-1 bring stage rows 16 (w & 1) .. + 15 of P, waves 2-3 those of Q; one
+  // load = 4 rows x 16 chunks, lane j -> row 4 i + (j >> 4), physical chunk j & 15
+  const bool isP = w < 2;
+  const uint16_t* base = isP ? pb.P : pb.Q;
+  const int ld = isP ? pb.ldp : pb.ldq;
+  const int ncols = isP ? pb.M : pb.Nc;
+  const int col0 = isP ? m0 : n0;
+  const int32_t* gather = isP ? nullptr : pb.row_index;
+  const int rb = 16 * (w & 1);  // first stage row of this wave
+  const uint32_t opoff = isP ? 0u : static_cast<uint32_t>(W2_OPB);
+  auto issue = [&](int s, int slot) {
+    // row indices: uniform addresses, so scalar loads, which the direct-to-LDS accounting
+    // (vector memory) does not see; rows past the segment are clamped to its last row and
+    // zeroed after landing
+    const int jr = j0 + s * W2_BK + rb;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int j = j0 + s * WG_BK + kb * 8 + r;
-      const bool ok = col_ok && j < j1;
-      okm |= ok ? (1u << r) : 0u;
-      row[r] = ok ? j : j0;  // a valid row: j0 < j1 whenever a stage exists
+    for (int i = 0; i < W2_DPW; ++i) {
+      const int sel = lane >> 4;
+      const int row = rb + 4 * i + sel;             // stage row
+      const int ja = min(jr + 4 * i, j1 - 1), jb = min(jr + 4 * i + 1, j1 - 1);
+      const int jc = min(jr + 4 * i + 2, j1 - 1), jd = min(jr + 4 * i + 3, j1 - 1);
+      int ra = ja, rbv = jb, rc = jc, rd = jd;
+      if (gather != nullptr) {
+        // the row index is read-only for the whole launch: constant address space, so the
+        // uniform loads become scalar loads
+        typedef const __attribute__((address_space(4))) int32_t cint;
+        cint* cg = (cint*)(gather);
+        ra = cg[ja];
+        rbv = cg[jb];
+        rc = cg[jc];
+        rd = cg[jd];
+      }
+      const int grow = sel == 0 ? ra : (sel == 1 ? rbv : (sel == 2 ? rc : rd));
+      const int c = w2_swz(row, lane & 15);         // logical chunk landing at lane & 15
+      int col = col0 + 8 * c;
+      if (col >= ncols) col = 0;                    // in bounds; such columns are never stored
+      const uint32_t off = static_cast<uint32_t>((static_cast<long>(grow) * ld + col) * 2);
+      w2_dma16(off, base, lds0 + slot * W2_STAGE + opoff + (rb + 4 * i) * W2_ROWB);
     }
-    if (gather != nullptr) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) row[r] = gather[row[r]];
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const u32x4*>(base + row[r] * ld);
   };
-  auto store = [&](const u32x4 (&v)[8], uint32_t okm) {
-    u32x4 z[8], o[8];
+
+  // fragment of the 32 columns [cb, cb + 32) of an operand for k16 step t: lane l holds
+  // column cb + (l & 31), stage rows 16 t + 8 (l >> 5) + 0..7
+  auto frag = [&](uint32_t opbase, int cb, int t) -> bf16x8 {
+    const int gq = lane >> 4, sl = lane & 15;
+    const int col = cb + 16 * (gq & 1) + 4 * (sl & 3);
+    const int u = col >> 2;
+    w2_v4s part[2];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) z[r] = ((okm >> r) & 1u) ? v[r] : u32x4{0u, 0u, 0u, 0u};
-    transpose8(z, o);
-    uint16_t* dst = isP ? sP : sQ;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *reinterpret_cast<u32x4*>(dst + (cb * 8 + c) * WG_LD + kb * 8) = o[c];
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * t + 8 * (gq >> 1) + 4 * h + (sl >> 2);
+      const int q = row & 3;
+      const uint32_t addr = opbase + row * W2_ROWB + ((u ^ (4 * q + 16 * (q & 1))) << 3);
+      part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((w2_lv4s*)((lds_char*)nullptr + addr));
+    }
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                      part[1][0], part[1][1], part[1][2], part[1][3]};
+    return __builtin_bit_cast(bf16x8, both);
   };
 
   floatx16 acc[2][2];
@@ -281,38 +320,39 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
-  u32x4 v[8];
-  uint32_t okm = 0;
-  if (nst > 0) {
-    load(0, v, okm);
-    store(v, okm);
-  }
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) load(s + 1, v, okm);  // in flight during the MFMAs
 #pragma unroll
-    for (int kk = 0; kk < WG_BK / 16; ++kk) {
+  for (int v = 0; v < W2_XS - 1; ++v)
+    if (v < nst) issue(v, v);
+  for (int s = 0; s < nst; ++s) {
+    // this stage's loads have landed (the later stages' may still be in flight)
+    if (s + 2 < nst) wait_vmcnt<W2_WAIT>();
+    else if (s + 1 < nst) wait_vmcnt<W2_DPW>();
+    else wait_vmcnt<0>();
+    const uint32_t sb = lds0 + (s % W2_XS) * W2_STAGE;
+    // rows past the segment (last stage only) read as zero
+    if (j0 + (s + 1) * W2_BK > j1) {
+      const int r = rb + (lane >> 2);
+      if (j0 + s * W2_BK + r >= j1) {
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        lds_u32x4* z = (lds_u32x4*)((lds_char*)nullptr + sb + opoff + r * W2_ROWB + (lane & 3) * 64);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    __syncthreads();  // publishes this stage; every wave is done with stage s - 1's slot
+    if (s + W2_XS - 1 < nst) issue(s + W2_XS - 1, (s + W2_XS - 1) % W2_XS);
+#pragma unroll
+    for (int t = 0; t < W2_BK / 16; ++t) {
       bf16x8 af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int m = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(sP + m * WG_LD + kk * 16 + (lane >> 5) * 8);
-      }
+      for (int i = 0; i < 2; ++i) af[i] = frag(sb, wm * 64 + i * 32, t);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int n = wn * 64 + jj * 32 + (lane & 31);
-        bf[jj] = *reinterpret_cast<const bf16x8*>(sQ + n * WG_LD + kk * 16 + (lane >> 5) * 8);
-      }
+      for (int jj = 0; jj < 2; ++jj) bf[jj] = frag(sb + W2_OPB, wn * 64 + jj * 32, t);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
-    }
-    if (s + 1 < nst) {
-      __syncthreads();  // every wave is done reading this stage
-      store(v, okm);
-      __syncthreads();
     }
   }
   // lane holds rows m = 8 (v / 4) + 4 (lane / 32) + v % 4 and column n = lane % 32
@@ -377,10 +417,14 @@ hipError_t launch_wgrad(int G, int M, int Nc, const void* P, int ldp, const void
   WgradProblem q1{static_cast<const uint16_t*>(P1), ldp1, static_cast<const uint16_t*>(Q1), ldq1,
                   nullptr, nullptr, rows1, out1 != nullptr ? 1 : 0, M1, Nc1, out1};
   auto tiles = [](const WgradProblem& q) -> long {
-    return static_cast<long>(q.G) * ((q.M + WG_BM - 1) / WG_BM) * ((q.Nc + WG_BN - 1) / WG_BN);
+    return static_cast<long>(q.G) * ((q.M + W2_BM - 1) / W2_BM) * ((q.Nc + W2_BN - 1) / W2_BN);
   };
   const long t0 = tiles(q0), t1 = out1 != nullptr ? tiles(q1) : 0;
   if (t0 + t1 <= 0) return hipSuccess;
+  // 32-bit byte offsets of the direct-to-LDS loads
+  auto fits = [](long rows_, int ld_) { return rows_ * ld_ * 2L < (1L << 32); };
+  if (!fits(rows, ldp) || !fits(rows, ldq) || (out1 != nullptr && (!fits(rows1, ldp1) || !fits(rows1, ldq1))))
+    return hipErrorNotSupported;
   if (t0 + t1 > 0x3fffffffL) return hipErrorInvalidValue;
   const long s_per = (t1 + 7) / 8, r_per = (t0 + 7) / 8;
   const long grid = 8 * (s_per + r_per);
