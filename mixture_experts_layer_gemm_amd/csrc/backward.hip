@@ -172,12 +172,15 @@ swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
 // those reads free of bank conflicts.
 constexpr int W2_BM = 128, W2_BN = 128;       // output tile
 constexpr int W2_BK = 32;                     // segment rows per stage
-constexpr int W2_XS = 4;                      // ring depth (stages)
+constexpr int W2_XS = 3;                      // ring depth (stages)
 constexpr int W2_ROWB = 256;                  // LDS bytes per stage row (128 bf16)
 constexpr int W2_OPB = W2_BK * W2_ROWB;       // bytes per operand per stage
 constexpr int W2_STAGE = 2 * W2_OPB;
 constexpr int W2_DPW = W2_STAGE / (1024 * 4); // direct-to-LDS loads per wave per stage
-constexpr int W2_WAIT = (W2_XS - 2) * W2_DPW; // the two later stages may be pending
+constexpr int W2_WAIT = (W2_XS - 2) * W2_DPW; // the later stages may be pending
+// epilogue rows per pass through the ring: the whole tile, or one 64-row half at a time
+constexpr int W2_EROWS = W2_XS * W2_STAGE >= W2_BM * W2_BN * 4 ? W2_BM : 64;
+static_assert(W2_XS * W2_STAGE >= W2_EROWS * W2_BN * 4, "the epilogue reuses the ring");
 static_assert(W2_DPW == 4, "each wave loads 16 rows of one operand per stage");
 
 struct WgradProblem {
@@ -208,7 +211,7 @@ __device__ __forceinline__ void w2_dma16(uint32_t voff, const void* sbase, uint3
 typedef short w2_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) w2_v4s w2_lv4s;
 
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   __shared__ __attribute__((aligned(1024))) char ring[W2_XS * W2_STAGE];
   typedef __attribute__((address_space(3))) char lds_char;
@@ -355,20 +358,40 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
     }
   }
-  // lane holds rows m = 8 (v / 4) + 4 (lane / 32) + v % 4 and column n = lane % 32
+  // epilogue through LDS (the ring is free once every wave is past the last stage), in
+  // passes of W2_EROWS tile rows: the rows go in as 128 fp32 each and leave as whole
+  // 16-byte row pieces. 4-float pieces are swizzled by 8 (row / 4 odd), so the two rows
+  // that one accumulator store writes (4 apart) fall 32 banks apart.
+  float* tileo = (float*)ring;
   float* out = pb.out + static_cast<size_t>(g) * pb.M * pb.Nc;
+  const int pc = tid & 31;  // 4-float column piece of this thread
+  const int n = n0 + 4 * pc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ps = 0; ps < W2_BM / W2_EROWS; ++ps) {
+    __syncthreads();
+    if (wm * 64 / W2_EROWS == ps) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-      if (n >= pb.Nc) continue;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
-        if (m < pb.M) out[static_cast<size_t>(m) * pb.Nc + n] = acc[i][jj][vv];
-      }
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int vv = 0; vv < 16; ++vv) {
+            // lane holds row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32 of the block
+            const int m = (wm * 64) % W2_EROWS + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+            const int nn = wn * 64 + jj * 32 + (lane & 31);
+            tileo[m * W2_BN + 4 * ((nn >> 2) ^ (8 * ((m >> 2) & 1))) + (nn & 3)] = acc[i][jj][vv];
+          }
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = tid >> 5; r < W2_EROWS; r += 8) {
+      const int m = m0 + ps * W2_EROWS + r;
+      // M and Nc are multiples of 64: a piece is wholly inside or wholly outside
+      if (m < pb.M && n < pb.Nc)
+        *reinterpret_cast<floatx4*>(out + static_cast<size_t>(m) * pb.Nc + n) =
+            *reinterpret_cast<const floatx4*>(tileo + r * W2_BN + 4 * (pc ^ (8 * ((r >> 2) & 1))));
+    }
+  }
 }
 
 }  // namespace
