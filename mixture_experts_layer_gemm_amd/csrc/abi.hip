@@ -236,6 +236,8 @@ static StreamProblem problem(const void* a, int a_rows, const int32_t* row_index
   p.w0 = static_cast<const uint16_t*>(w0);
   p.w1 = static_cast<const uint16_t*>(w1);
   p.out = static_cast<uint16_t*>(out);
+  p.dh = nullptr;
+  p.dab = nullptr;
   return p;
 }
 
@@ -573,19 +575,6 @@ int moe_backward(const moe_backward_args* a, void* workspace, size_t workspace_b
   // upstream rows: dF = r dy in the packed expert order, dG = s dy
   MOE_HIP(launch_grad_rows(T, d, K, a->dy, a->dest_row, a->topk_r, a->s, a->s_tok, w.dF,
                            sh ? w.dG : nullptr, stream));
-  // recompute A and B (rows gathered from x, as in the forward)
-  {
-    const StreamProblem pa = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_gate,
-                                     nullptr, w.A);
-    const StreamProblem pas = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_gate, nullptr,
-                                      w.As);
-    MOE_HIP(plain_pair(pa, sh ? &pas : nullptr, stream));
-    const StreamProblem pb = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_up,
-                                     nullptr, w.B);
-    const StreamProblem pbs = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_up, nullptr,
-                                      w.Bs);
-    MOE_HIP(plain_pair(pb, sh ? &pbs : nullptr, stream));
-  }
   // dH = dF W_d
   {
     const StreamProblem p0 = problem(w.dF, R, nullptr, a->offsets, N, R, d, dr, a->wt_down,
@@ -594,10 +583,38 @@ int moe_backward(const moe_backward_args* a, void* workspace, size_t workspace_b
                                      w.dHs);
     MOE_HIP(plain_pair(p0, sh ? &p1 : nullptr, stream));
   }
-  // SwiGLU backward: [dA | dB] and H
-  if (R > 0)
-    MOE_HIP(launch_swiglu_bwd(R, a->offsets + N, dr, w.dH, w.A, w.B, w.dAB, w.H, stream));
-  if (sh) MOE_HIP(launch_swiglu_bwd(T, nullptr, ds, w.dHs, w.As, w.Bs, w.dABs, w.Hs, stream));
+  // recompute A and B (rows gathered from x, as in the forward) and take the SwiGLU
+  // backward: [dA | dB] and H. One persistent launch does both for the routed experts and
+  // the shared MLP where the shapes fit it; otherwise A and B go through memory.
+  {
+    StreamProblem f0 = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_gate,
+                               a->w_up, w.H);
+    f0.dh = w.dH;
+    f0.dab = w.dAB;
+    StreamProblem f1{};
+    if (sh) {
+      f1 = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_gate, a->ws_up, w.Hs);
+      f1.dh = w.dHs;
+      f1.dab = w.dABs;
+    }
+    if (stream_swiglu_bwd_supported(f0, f1)) {
+      MOE_HIP(launch_stream_swiglu_bwd(f0, f1, stream));
+    } else {
+      const StreamProblem pa = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr,
+                                       a->w_gate, nullptr, w.A);
+      const StreamProblem pas = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_gate,
+                                        nullptr, w.As);
+      MOE_HIP(plain_pair(pa, sh ? &pas : nullptr, stream));
+      const StreamProblem pb = problem(a->x, T, a->row_token, a->offsets, N, R, d, dr, a->w_up,
+                                       nullptr, w.B);
+      const StreamProblem pbs = problem(a->x, T, nullptr, nullptr, 1, T, d, ds, a->ws_up,
+                                        nullptr, w.Bs);
+      MOE_HIP(plain_pair(pb, sh ? &pbs : nullptr, stream));
+      if (R > 0)
+        MOE_HIP(launch_swiglu_bwd(R, a->offsets + N, dr, w.dH, w.A, w.B, w.dAB, w.H, stream));
+      if (sh) MOE_HIP(launch_swiglu_bwd(T, nullptr, ds, w.dHs, w.As, w.Bs, w.dABs, w.Hs, stream));
+    }
+  }
   // dX = [dA dB] [W_g; W_u], then dx = sum over kept routes + shared
   {
     const StreamProblem p0 = problem(w.dAB, R, nullptr, a->offsets, N, R, 2 * dr, d,

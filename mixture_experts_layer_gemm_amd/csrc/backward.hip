@@ -164,7 +164,7 @@ swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
 // ---- weight gradients: out[g][m][n] = sum_{j in segment g} P[j][m] Q[row(j)][n] ---------
 // Both operands are k-major (k = the row j of a segment), while v_mfma_f32_32x32x16_bf16
 // wants 8 consecutive k of one column per lane. The rows go to LDS as they are, by
-// direct-to-LDS loads into a 4-stage ring (32 rows per stage), and the fragments come out
+// direct-to-LDS loads into a ring of W2_XS stages (32 rows each), and the fragments come out
 // with ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i & 3 of the
 // 8-byte pieces that lanes (i >> 2), 4 + (i >> 2), 8 + (i >> 2), 12 + (i >> 2) of the
 // group point at; pointing lane s at column block 4 (s & 3) of row s >> 2 therefore hands

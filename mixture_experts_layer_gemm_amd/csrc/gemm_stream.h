@@ -19,6 +19,10 @@ struct StreamProblem {
   const uint16_t* w0;
   const uint16_t* w1;         // SwiGLU only
   uint16_t* out;              // [rows][Nd]
+  // SwiGLU backward only (else NULL): dh [rows][Nd] is the gradient of the SwiGLU
+  // output; the launch writes out = SiLU(A) B and dab [rows][2 Nd] = [dA | dB]
+  const uint16_t* dh;
+  uint16_t* dab;
 };
 
 // Whether one persistent launch can run p0 (grouped or dense) together with p1 (dense,
@@ -28,3 +32,9 @@ bool stream_gemm_supported(bool swiglu, const StreamProblem& p0, const StreamPro
 // Enqueues p0 and p1 as one launch; hipErrorNotSupported when the shapes do not fit.
 hipError_t launch_stream_gemm(bool swiglu, const StreamProblem& p0, const StreamProblem& p1,
                               hipStream_t stream);
+
+// The SwiGLU backward with the gate and up products recomputed: for each problem, with
+// A = a W0^T and B = a W1^T, writes out = SiLU(A) B, dab = [dH B SiLU'(A) | dH SiLU(A)].
+bool stream_swiglu_bwd_supported(const StreamProblem& p0, const StreamProblem& p1);
+hipError_t launch_stream_swiglu_bwd(const StreamProblem& p0, const StreamProblem& p1,
+                                    hipStream_t stream);

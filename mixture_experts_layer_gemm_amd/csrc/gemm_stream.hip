@@ -103,16 +103,25 @@ struct SkTile {
   int nst;   // k stages
 };
 
-template <int NBW, int XBM, int RS, bool SWIGLU>
+// MODE: SK_PLAIN, SK_SWIGLU, or SK_SWIGLU_BWD (gate and up products as in SK_SWIGLU; the
+// epilogue takes dH and writes H = SiLU(A) B and [dA | dB] instead of SiLU(A) B alone)
+constexpr int SK_PLAIN = 0, SK_SWIGLU = 1, SK_SWIGLU_BWD = 2;
+
+template <int NBW, int XBM, int RS, int MODE>
 __global__ void __launch_bounds__(SK_THREADS, 1)
 gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   using C = SK<NBW, XBM, RS>;
+  constexpr bool SWIGLU = MODE != SK_PLAIN;
   constexpr int COLS = SWIGLU ? C::COLS_SWIGLU : C::COLS_PLAIN;
   __shared__ int s_off[kMaxN + 2];     // packed row offsets of the groups (p1 last)
   __shared__ int s_tstart[SK_THREADS + 1];
   __shared__ int s_cstart[SK_THREADS + 1];
   __shared__ int s_rows[2][256];       // gathered activation rows of the current / next tile
   __shared__ __attribute__((aligned(1024))) char lds[SK_XS * C::XSTAGE];
+  // SwiGLU backward: the tile's dH rows ([BM][COLS] bf16, 16-byte chunks of row r permuted
+  // by r & 15), brought in by direct-to-LDS loads during the tile's last stage
+  constexpr int DH_ROWB = COLS * 2;
+  __shared__ __attribute__((aligned(1024))) char dhbuf[MODE == SK_SWIGLU_BWD ? C::BM * DH_ROWB : 16];
   typedef __attribute__((address_space(3))) char lds_char;
   const int tid = threadIdx.x;
   const int G0 = p0.G;
@@ -187,6 +196,7 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds_base = static_cast<uint32_t>((size_t)((lds_char*)lds));
   const uint32_t rows_base = static_cast<uint32_t>((size_t)((lds_char*)(&s_rows[0][0])));
+  const uint32_t dh_base = static_cast<uint32_t>((size_t)((lds_char*)dhbuf));
 
   auto tile_at = [&](int ti) -> SkTile {
     int lo = 0, hi = NG - 1;  // largest g with s_tstart[g] <= ti (a non-empty group)
@@ -259,6 +269,23 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     }
   };
 
+  // dH of tile k into dhbuf: wave w brings tile rows 32 w .. 32 w + 31 (rows past the tile
+  // repeat its last row), lane j of load i row 32 w + 4 i + (j >> 4), chunk j & 15
+  auto issue_dh = [&](const SkTile& k) {
+    static_assert(MODE != SK_SWIGLU_BWD || (C::BM == 128 && DH_ROWB == 256),
+                  "dH staging assumes 128 rows of 256 bytes");
+    const StreamProblem& P = prob(k);
+    const uint32_t rowb = static_cast<uint32_t>(P.Nd) * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 32 * w + 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (rr & 15);
+      const uint32_t off = static_cast<uint32_t>(k.row0 + min(rr, k.rows - 1)) * rowb +
+                           static_cast<uint32_t>(k.n0 + 8 * c) * 2u;
+      sk_dma16(off, P.dh, dh_base + (32 * w + 4 * i) * DH_ROWB);
+    }
+  };
+
   SkTile cur = tile_at(t);
   bool has_n = t + step < t_end;
   SkTile nxt = has_n ? tile_at(t + step) : cur;
@@ -319,6 +346,10 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
         // slot that stage s + XS - 1 overwrites
         wait_vmcnt<C::WAITN>();
         __syncthreads();
+        // (the previous tile's epilogue read of dhbuf is behind this barrier)
+        if constexpr (MODE == SK_SWIGLU_BWD) {
+          if (s == nst - 1) issue_dh(cur);
+        }
         {
           const int ts = s + SK_XS - 1;
           uint32_t xr[C::XDPW];
@@ -372,42 +403,89 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     // epilogue: lane (lr, lh) holds row 32 j + lr, columns 8 q + 4 lh + {0..3} of each
     // 32-wide block; one exchange between lane halves gives each lane two 16-byte pieces
     // per row and block (columns 8 lh..+7 and 16 + 8 lh..+7)
+    if constexpr (MODE == SK_SWIGLU_BWD) {
+      // the last stage issued exactly PER loads after the dH loads
+      wait_vmcnt<C::PER>();
+      __syncthreads();
+    }
     {
       const StreamProblem& P = prob(cur);
       constexpr int OB = SWIGLU ? NBW / 2 : NBW;  // output blocks per wave
+      // packed bf16 pieces pk[q] (columns 8 q + 4 lh + {0..3}) -> row dst, columns n..n+31
+      auto put = [&](const u32x2* pk, uint16_t* dst, bool ok) {
+        // lh = 0 keeps q = 0, 2 and receives the partner's; lh = 1 keeps q = 1, 3
+        const u32x2 s0v = lh ? pk[0] : pk[1], s1v = lh ? pk[2] : pk[3];
+        u32x2 r0, r1;
+        r0[0] = __shfl_xor(s0v[0], 32, kWave);
+        r0[1] = __shfl_xor(s0v[1], 32, kWave);
+        r1[0] = __shfl_xor(s1v[0], 32, kWave);
+        r1[1] = __shfl_xor(s1v[1], 32, kWave);
+        const u32x4 ca = lh ? u32x4{r0[0], r0[1], pk[1][0], pk[1][1]}
+                            : u32x4{pk[0][0], pk[0][1], r0[0], r0[1]};
+        const u32x4 cb = lh ? u32x4{r1[0], r1[1], pk[3][0], pk[3][1]}
+                            : u32x4{pk[2][0], pk[2][1], r1[0], r1[1]};
+        if (ok) {
+          *reinterpret_cast<u32x4*>(dst + 8 * lh) = ca;
+          *reinterpret_cast<u32x4*>(dst + 16 + 8 * lh) = cb;
+        }
+      };
 #pragma unroll
       for (int j = 0; j < XBM; ++j) {
         if (j >= xb) break;
         const int m = 32 * j + lr;
         const bool ok = m < cur.rows;
-        uint16_t* orow = P.out + static_cast<size_t>(cur.row0 + (ok ? m : 0)) * P.Nd;
+        const size_t prow = static_cast<size_t>(cur.row0 + (ok ? m : 0));
+        uint16_t* orow = P.out + prow * P.Nd;
 #pragma unroll
         for (int ob = 0; ob < OB; ++ob) {
-          u32x2 pk[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              h[e] = SWIGLU ? silu_f(acc[ob][j][4 * q + e]) * acc[ob + NBW / 2][j][4 * q + e]
-                            : acc[ob][j][4 * q + e];
-            pk[q] = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-          }
-          // lh = 0 keeps q = 0, 2 and receives the partner's; lh = 1 keeps q = 1, 3
-          const u32x2 s0v = lh ? pk[0] : pk[1], s1v = lh ? pk[2] : pk[3];
-          u32x2 r0, r1;
-          r0[0] = __shfl_xor(s0v[0], 32, kWave);
-          r0[1] = __shfl_xor(s0v[1], 32, kWave);
-          r1[0] = __shfl_xor(s1v[0], 32, kWave);
-          r1[1] = __shfl_xor(s1v[1], 32, kWave);
-          const u32x4 ca = lh ? u32x4{r0[0], r0[1], pk[1][0], pk[1][1]}
-                              : u32x4{pk[0][0], pk[0][1], r0[0], r0[1]};
-          const u32x4 cb = lh ? u32x4{r1[0], r1[1], pk[3][0], pk[3][1]}
-                              : u32x4{pk[2][0], pk[2][1], r1[0], r1[1]};
           const int n = cur.n0 + 32 * (SWIGLU ? w * (NBW / 2) + ob : w * NBW + ob);
-          if (ok) {
-            *reinterpret_cast<u32x4*>(orow + n + 8 * lh) = ca;
-            *reinterpret_cast<u32x4*>(orow + n + 16 + 8 * lh) = cb;
+          if constexpr (MODE == SK_SWIGLU_BWD) {
+            // dH of this lane's 16 elements (from dhbuf); A, B are the fp32 sums
+            u32x2 gh[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = (n - cur.n0) / 8 + q;  // logical 16-byte chunk of the tile row
+              gh[q] = *reinterpret_cast<const u32x2*>(dhbuf + m * DH_ROWB +
+                                                      ((c ^ (m & 15)) << 4) + 8 * lh);
+            }
+            uint16_t* abrow = P.dab + prow * 2 * P.Nd + n;
+            // H = SiLU(A) B (as the forward's SwiGLU epilogue), dA = dH B sg (1 + A (1 - sg)),
+            // dB = dH A sg, with sg = sigmoid(A)
+            u32x2 ph[4], pa[4], pb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float oh[4], oa[4], ob2[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float a = acc[ob][j][4 * q + e];
+                const float b = acc[ob + NBW / 2][j][4 * q + e];
+                const uint32_t gw = gh[q][e >> 1];
+                const float g = __uint_as_float((e & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+                const float sa = a * sg;
+                oh[e] = sa * b;
+                oa[e] = g * b * sg * (1.0f + a * (1.0f - sg));
+                ob2[e] = g * sa;
+              }
+              ph[q] = u32x2{pack_bf16x2(oh[0], oh[1]), pack_bf16x2(oh[2], oh[3])};
+              pa[q] = u32x2{pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3])};
+              pb[q] = u32x2{pack_bf16x2(ob2[0], ob2[1]), pack_bf16x2(ob2[2], ob2[3])};
+            }
+            put(ph, orow + n, ok);
+            put(pa, abrow, ok);
+            put(pb, abrow + P.Nd, ok);
+          } else {
+            u32x2 pk[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                h[e] = SWIGLU ? silu_f(acc[ob][j][4 * q + e]) * acc[ob + NBW / 2][j][4 * q + e]
+                              : acc[ob][j][4 * q + e];
+              pk[q] = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+            }
+            put(pk, orow + n, ok);
           }
           __builtin_amdgcn_sched_barrier(0);  // one block's values live at a time
         }
@@ -433,8 +511,10 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
 // tile shape: 2 weight blocks per wave, 128 rows, 4 stages of weights in flight
 constexpr int kNBW = 2, kXBM = 4, kRS = 4;
 
-bool fits(bool swiglu, const StreamProblem& P) {
+bool fits(int mode, const StreamProblem& P) {
+  const bool swiglu = mode != SK_PLAIN;
   if (P.rows <= 0) return true;
+  if (mode == SK_SWIGLU_BWD && (P.dh == nullptr || P.dab == nullptr)) return false;
   using C = SK<kNBW, kXBM, kRS>;
   const int cols = swiglu ? C::COLS_SWIGLU : C::COLS_PLAIN;
   const int nst = P.Kd / SK_BKX;
@@ -446,20 +526,21 @@ bool fits(bool swiglu, const StreamProblem& P) {
   const long a_rows = P.row_index != nullptr ? P.a_rows : P.rows;
   if (a_rows <= 0 || a_rows * P.Kd * 2L >= (1L << 32)) return false;
   if (P.rows * 4L >= (1L << 32)) return false;
+  if (mode == SK_SWIGLU_BWD && P.rows * P.Nd * 2L >= (1L << 32)) return false;  // dH offsets
   return true;
 }
 
 }  // namespace
 
-bool stream_gemm_supported(bool swiglu, const StreamProblem& p0, const StreamProblem& p1) {
-  if (p0.rows <= 0 || !fits(swiglu, p0) || !fits(swiglu, p1)) return false;
+static bool supported(int mode, const StreamProblem& p0, const StreamProblem& p1) {
+  if (p0.rows <= 0 || !fits(mode, p0) || !fits(mode, p1)) return false;
   if (p1.rows > 0 && (p1.offsets != nullptr || p1.G != 1 || p0.G + 1 > SK_THREADS)) return false;
   return true;
 }
 
-hipError_t launch_stream_gemm(bool swiglu, const StreamProblem& p0, const StreamProblem& p1,
-                              hipStream_t stream) {
-  if (!stream_gemm_supported(swiglu, p0, p1)) return hipErrorNotSupported;
+static hipError_t launch(int mode, const StreamProblem& p0, const StreamProblem& p1,
+                         hipStream_t stream) {
+  if (!supported(mode, p0, p1)) return hipErrorNotSupported;
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
@@ -471,11 +552,32 @@ hipError_t launch_stream_gemm(bool swiglu, const StreamProblem& p0, const Stream
   }
   const int grid = cus[dev] / 8 * 8;
   if (grid <= 0) return hipErrorNotSupported;
-  if (swiglu)
-    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, true>), dim3(grid), dim3(SK_THREADS),
-                       0, stream, p0, p1);
+  if (mode == SK_SWIGLU)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_SWIGLU>), dim3(grid),
+                       dim3(SK_THREADS), 0, stream, p0, p1);
+  else if (mode == SK_SWIGLU_BWD)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_SWIGLU_BWD>), dim3(grid),
+                       dim3(SK_THREADS), 0, stream, p0, p1);
   else
-    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, false>), dim3(grid), dim3(SK_THREADS),
-                       0, stream, p0, p1);
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_PLAIN>), dim3(grid),
+                       dim3(SK_THREADS), 0, stream, p0, p1);
   return hipGetLastError();
+}
+
+bool stream_gemm_supported(bool swiglu, const StreamProblem& p0, const StreamProblem& p1) {
+  return supported(swiglu ? SK_SWIGLU : SK_PLAIN, p0, p1);
+}
+
+hipError_t launch_stream_gemm(bool swiglu, const StreamProblem& p0, const StreamProblem& p1,
+                              hipStream_t stream) {
+  return launch(swiglu ? SK_SWIGLU : SK_PLAIN, p0, p1, stream);
+}
+
+bool stream_swiglu_bwd_supported(const StreamProblem& p0, const StreamProblem& p1) {
+  return supported(SK_SWIGLU_BWD, p0, p1);
+}
+
+hipError_t launch_stream_swiglu_bwd(const StreamProblem& p0, const StreamProblem& p1,
+                                    hipStream_t stream) {
+  return launch(SK_SWIGLU_BWD, p0, p1, stream);
 }
