@@ -10,9 +10,9 @@
 // d_model reduction split round-robin over the waves in 32-wide steps, operands loaded
 // straight from global memory into the MFMA lane layout several steps at a time (x is
 // streamed once; W_r stays in L2), and the per-wave partial tiles summed in LDS in a
-// fixed order. Phase 2 gives each wave BT / waves tokens: top-K by K rounds of a
-// wave-wide max over packed (ordered float key, inverted expert index) 64-bit values,
-// which yields the lowest index on ties, then the coefficients in the lanes k < K.
+// fixed order. Phase 2 gives each wave BT / waves tokens: top-K by ranks of packed
+// (ordered float key, inverted expert index) 64-bit values, which put the lowest index
+// first on ties, then the coefficients in the lanes k < K.
 //
 // Auxiliary-loss-free balancing ("Section 10: Routing, Capacity, and Load Balancing",
 // Eq. 35): with a persistent expert bias b the keys become z + b (softmax rules) or
@@ -204,9 +204,15 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
 
   // ---- phase 2: top-K and coefficients, one wave per token --------------------------
+  // Selection by rank: every expert's packed key goes to LDS, each lane counts the keys
+  // above each of its own (all comparisons independent, no cross-lane chains), and the
+  // expert of rank k < K lands in slot k. Equal float keys are ordered by the packed
+  // inverted index, so the lower index ranks first.
   const int lane = tid & 63;
   const int w = tid >> 6;
   const bool biased = sel_bias != nullptr;
+  __shared__ uint64_t s_key[WAVES][kMaxN];
+  __shared__ int s_sel[WAVES][kMaxK];
   float bias_r[kMaxN / kWave];
 #pragma unroll
   for (int j = 0; j < kMaxN / kWave; ++j) {
@@ -217,35 +223,37 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
     const int tok = t0 + t;
     if (tok >= T) break;
     const float* zr = z + t * ldz;
-    uint64_t cand[kMaxN / kWave];
+    uint64_t mine[kMaxN / kWave];
 #pragma unroll
     for (int j = 0; j < kMaxN / kWave; ++j) {
       const int e = lane + j * kWave;
-      float key = 0.f;
+      mine[j] = 0ull;
       if (e < N) {
-        key = zr[e];
+        float key = zr[e];
         if (biased) key = (score == 1 ? sigmoid_f(key) : key) + bias_r[j];
+        mine[j] = (static_cast<uint64_t>(ord_key(key)) << 32) |
+                  static_cast<uint64_t>(~static_cast<uint32_t>(e));
+        s_key[w][e] = mine[j];
       }
-      cand[j] = (e < N) ? ((static_cast<uint64_t>(ord_key(key)) << 32) |
-                           static_cast<uint64_t>(~static_cast<uint32_t>(e)))
-                        : 0ull;
     }
-    float selz = 0.f;
-    int sele = 0;
-    for (int k = 0; k < K; ++k) {
-      uint64_t m = cand[0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int j = 1; j < kMaxN / kWave; ++j) m = cand[j] > m ? cand[j] : m;
-      m = wave_max_u64(m);
-      const int e = static_cast<int>(~static_cast<uint32_t>(m));
-      if (lane == k) {
-        selz = biased ? zr[e] : unord_key(static_cast<uint32_t>(m >> 32));
-        sele = e;
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxN / kWave; ++j)
-        if (e == lane + j * kWave) cand[j] = 0ull;
+    for (int j = 0; j < kMaxN / kWave; ++j) {
+      if (j * kWave >= N) break;  // uniform
+      int rank = 0;
+#pragma unroll 8
+      for (int i = 0; i < N; ++i)
+        rank += s_key[w][i] > mine[j] ? 1 : 0;  // one address for all lanes: a broadcast
+      const int e = lane + j * kWave;
+      if (e < N && rank < K) s_sel[w][rank] = e;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int sele = lane < K ? s_sel[w][lane] : 0;
+    const float selz = lane < K ? zr[sele] : 0.f;
     const bool act = lane < K;
     float r;
     if (score == 1) {  // sigmoid affinities
