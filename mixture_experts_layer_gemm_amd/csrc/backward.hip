@@ -170,18 +170,20 @@ swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
 // group point at; pointing lane s at column block 4 (s & 3) of row s >> 2 therefore hands
 // lane i four consecutive rows of one column. An 8-byte-unit XOR swizzle per row keeps
 // those reads free of bank conflicts.
-constexpr int W2_BM = 128, W2_BN = 128;       // output tile
+constexpr int W2_BM = 256, W2_BN = 128;       // output tile (M: P columns, N: Q columns)
 constexpr int W2_BK = 32;                     // segment rows per stage
 constexpr int W2_XS = 3;                      // ring depth (stages)
-constexpr int W2_ROWB = 256;                  // LDS bytes per stage row (128 bf16)
-constexpr int W2_OPB = W2_BK * W2_ROWB;       // bytes per operand per stage
-constexpr int W2_STAGE = 2 * W2_OPB;
-constexpr int W2_DPW = W2_STAGE / (1024 * 4); // direct-to-LDS loads per wave per stage
+constexpr int W2_ROWP = W2_BM * 2;            // LDS bytes per stage row of P (256 bf16)
+constexpr int W2_ROWQ = W2_BN * 2;            // LDS bytes per stage row of Q (128 bf16)
+constexpr int W2_OPP = W2_BK * W2_ROWP;       // bytes of P per stage
+constexpr int W2_STAGE = W2_BK * (W2_ROWP + W2_ROWQ);
+constexpr int W2_DPP = W2_OPP / (1024 * 4);   // direct-to-LDS loads of P per wave per stage
+constexpr int W2_DPQ = W2_BK * W2_ROWQ / (1024 * 4);
+constexpr int W2_DPW = W2_DPP + W2_DPQ;       // loads per wave per stage
 constexpr int W2_WAIT = (W2_XS - 2) * W2_DPW; // the later stages may be pending
-// epilogue rows per pass through the ring: the whole tile, or one 64-row half at a time
-constexpr int W2_EROWS = W2_XS * W2_STAGE >= W2_BM * W2_BN * 4 ? W2_BM : 64;
+constexpr int W2_EROWS = 64;                  // epilogue rows per pass through the ring
 static_assert(W2_XS * W2_STAGE >= W2_EROWS * W2_BN * 4, "the epilogue reuses the ring");
-static_assert(W2_DPW == 4, "each wave loads 16 rows of one operand per stage");
+static_assert(W2_DPP == 4 && W2_DPQ == 2, "each wave loads 8 rows of each operand per stage");
 
 struct WgradProblem {
   const uint16_t* P;      // [rows][ldp], columns [0, M) used
@@ -195,7 +197,8 @@ struct WgradProblem {
   float* out;             // [G][M][Nc]
 };
 
-// physical 16-byte chunk of logical chunk c (0..15) in stage row r
+// physical 16-byte chunk of logical chunk c in stage row r (the low 4 bits are permuted,
+// so the map stays inside every 16-chunk block of a row)
 __device__ __forceinline__ int w2_swz(int r, int c) {
   const int q = r & 3;
   return c ^ (2 * q + 8 * (q & 1));
@@ -211,7 +214,7 @@ __device__ __forceinline__ void w2_dma16(uint32_t voff, const void* sbase, uint3
 typedef short w2_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) w2_v4s w2_lv4s;
 
-__global__ void __launch_bounds__(256, 3)
+__global__ void __launch_bounds__(256, 2)
 wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   __shared__ __attribute__((aligned(1024))) char ring[W2_XS * W2_STAGE];
   typedef __attribute__((address_space(3))) char lds_char;
@@ -253,26 +256,31 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
   const uint32_t lds0 = static_cast<uint32_t>((size_t)((lds_char*)ring));
+  const int32_t* gather = pb.row_index;
+  const int rb = 8 * w;  // wave w brings stage rows rb .. rb + 7 of both operands
 
-  // loads: waves 0-1 bring stage rows 16 (w & 1) .. + 15 of P, waves 2-3 those of Q; one
-  // load = 4 rows x 16 chunks, lane j -> row 4 i + (j >> 4), physical chunk j & 15
-  const bool isP = w < 2;
-  const uint16_t* base = isP ? pb.P : pb.Q;
-  const int ld = isP ? pb.ldp : pb.ldq;
-  const int ncols = isP ? pb.M : pb.Nc;
-  const int col0 = isP ? m0 : n0;
-  const int32_t* gather = isP ? nullptr : pb.row_index;
-  const int rb = 16 * (w & 1);  // first stage row of this wave
-  const uint32_t opoff = isP ? 0u : static_cast<uint32_t>(W2_OPB);
+  // one stage: P rows as 2 rows x 32 chunks per load (lane j -> row rb + 2 i + (j >> 5),
+  // physical chunk j & 31), Q rows as 4 rows x 16 chunks (row rb + 4 i + (j >> 4),
+  // physical chunk j & 15); rows past the segment are clamped to its last row and zeroed
+  // after landing, columns past the matrix read column 0 and are never stored
   auto issue = [&](int s, int slot) {
-    // row indices: uniform addresses, so scalar loads, which the direct-to-LDS accounting
-    // (vector memory) does not see; rows past the segment are clamped to its last row and
-    // zeroed after landing
     const int jr = j0 + s * W2_BK + rb;
+    const uint32_t sb = lds0 + slot * W2_STAGE;
 #pragma unroll
-    for (int i = 0; i < W2_DPW; ++i) {
+    for (int i = 0; i < W2_DPP; ++i) {
+      const int row = rb + 2 * i + (lane >> 5);
+      const int grow = min(jr + 2 * i + (lane >> 5), j1 - 1);
+      int col = m0 + 8 * w2_swz(row, lane & 31);
+      if (col >= pb.M) col = 0;
+      const uint32_t off = static_cast<uint32_t>((static_cast<long>(grow) * pb.ldp + col) * 2);
+      w2_dma16(off, pb.P, sb + (rb + 2 * i) * W2_ROWP);
+    }
+#pragma unroll
+    for (int i = 0; i < W2_DPQ; ++i) {
+      // row indices: uniform addresses, so scalar loads, which the direct-to-LDS
+      // accounting (vector memory) does not see
       const int sel = lane >> 4;
-      const int row = rb + 4 * i + sel;             // stage row
+      const int row = rb + 4 * i + sel;
       const int ja = min(jr + 4 * i, j1 - 1), jb = min(jr + 4 * i + 1, j1 - 1);
       const int jc = min(jr + 4 * i + 2, j1 - 1), jd = min(jr + 4 * i + 3, j1 - 1);
       int ra = ja, rbv = jb, rc = jc, rd = jd;
@@ -287,17 +295,16 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
         rd = cg[jd];
       }
       const int grow = sel == 0 ? ra : (sel == 1 ? rbv : (sel == 2 ? rc : rd));
-      const int c = w2_swz(row, lane & 15);         // logical chunk landing at lane & 15
-      int col = col0 + 8 * c;
-      if (col >= ncols) col = 0;                    // in bounds; such columns are never stored
-      const uint32_t off = static_cast<uint32_t>((static_cast<long>(grow) * ld + col) * 2);
-      w2_dma16(off, base, lds0 + slot * W2_STAGE + opoff + (rb + 4 * i) * W2_ROWB);
+      int col = n0 + 8 * w2_swz(row, lane & 15);
+      if (col >= pb.Nc) col = 0;
+      const uint32_t off = static_cast<uint32_t>((static_cast<long>(grow) * pb.ldq + col) * 2);
+      w2_dma16(off, pb.Q, sb + W2_OPP + (rb + 4 * i) * W2_ROWQ);
     }
   };
 
-  // fragment of the 32 columns [cb, cb + 32) of an operand for k16 step t: lane l holds
-  // column cb + (l & 31), stage rows 16 t + 8 (l >> 5) + 0..7
-  auto frag = [&](uint32_t opbase, int cb, int t) -> bf16x8 {
+  // fragment of the 32 columns [cb, cb + 32) of an operand (rows of rowb bytes) for k16
+  // step t: lane l holds column cb + (l & 31), stage rows 16 t + 8 (l >> 5) + 0..7
+  auto frag = [&](uint32_t opbase, int rowb, int cb, int t) -> bf16x8 {
     const int gq = lane >> 4, sl = lane & 15;
     const int col = cb + 16 * (gq & 1) + 4 * (sl & 3);
     const int u = col >> 2;
@@ -306,7 +313,7 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     for (int h = 0; h < 2; ++h) {
       const int row = 16 * t + 8 * (gq >> 1) + 4 * h + (sl >> 2);
       const int q = row & 3;
-      const uint32_t addr = opbase + row * W2_ROWB + ((u ^ (4 * q + 16 * (q & 1))) << 3);
+      const uint32_t addr = opbase + row * rowb + ((u ^ (4 * q + 16 * (q & 1))) << 3);
       part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((w2_lv4s*)((lds_char*)nullptr + addr));
     }
     typedef short v8s __attribute__((ext_vector_type(8)));
@@ -315,9 +322,11 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     return __builtin_bit_cast(bf16x8, both);
   };
 
-  floatx16 acc[2][2];
+  // wave (wm, wn) owns tile rows wm * 128 .. + 127 (4 blocks of 32) and columns
+  // wn * 64 .. + 63 (2 blocks of 32)
+  floatx16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -332,36 +341,39 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     else if (s + 1 < nst) wait_vmcnt<W2_DPW>();
     else wait_vmcnt<0>();
     const uint32_t sb = lds0 + (s % W2_XS) * W2_STAGE;
-    // rows past the segment (last stage only) read as zero
+    // rows past the segment (last stage only) read as zero: each wave clears its own rows
     if (j0 + (s + 1) * W2_BK > j1) {
-      const int r = rb + (lane >> 2);
+      const int r = rb + (lane >> 3);
       if (j0 + s * W2_BK + r >= j1) {
         typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-        lds_u32x4* z = (lds_u32x4*)((lds_char*)nullptr + sb + opoff + r * W2_ROWB + (lane & 3) * 64);
+        lds_u32x4* zp = (lds_u32x4*)((lds_char*)nullptr + sb + r * W2_ROWP + (lane & 7) * 64);
+        lds_u32x4* zq = (lds_u32x4*)((lds_char*)nullptr + sb + W2_OPP + r * W2_ROWQ + (lane & 7) * 32);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < 4; ++c) zp[c] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) zq[c] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     __syncthreads();  // publishes this stage; every wave is done with stage s - 1's slot
     if (s + W2_XS - 1 < nst) issue(s + W2_XS - 1, (s + W2_XS - 1) % W2_XS);
 #pragma unroll
     for (int t = 0; t < W2_BK / 16; ++t) {
-      bf16x8 af[2], bf[2];
+      bf16x8 af[4], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = frag(sb, wm * 64 + i * 32, t);
+      for (int i = 0; i < 4; ++i) af[i] = frag(sb, W2_ROWP, wm * 128 + i * 32, t);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) bf[jj] = frag(sb + W2_OPB, wn * 64 + jj * 32, t);
+      for (int jj = 0; jj < 2; ++jj) bf[jj] = frag(sb + W2_OPP, W2_ROWQ, wn * 64 + jj * 32, t);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
     }
   }
   // epilogue through LDS (the ring is free once every wave is past the last stage), in
-  // passes of W2_EROWS tile rows: the rows go in as 128 fp32 each and leave as whole
-  // 16-byte row pieces. 4-float pieces are swizzled by 8 (row / 4 odd), so the two rows
-  // that one accumulator store writes (4 apart) fall 32 banks apart.
+  // passes of 64 tile rows: the rows go in as 128 fp32 each and leave as whole 16-byte
+  // row pieces. 4-float pieces are swizzled by 8 (row / 4 odd), so the two rows that one
+  // accumulator store writes (4 apart) fall 32 banks apart.
   float* tileo = (float*)ring;
   float* out = pb.out + static_cast<size_t>(g) * pb.M * pb.Nc;
   const int pc = tid & 31;  // 4-float column piece of this thread
@@ -369,18 +381,22 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
 #pragma unroll
   for (int ps = 0; ps < W2_BM / W2_EROWS; ++ps) {
     __syncthreads();
-    if (wm * 64 / W2_EROWS == ps) {
+    // pass ps holds tile rows 64 ps .. + 63: blocks i = 2 (ps & 1) + {0, 1} of the waves
+    // with wm = ps / 2
+    if (wm == ps / 2) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * (ps & 1) + ii;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int vv = 0; vv < 16; ++vv) {
             // lane holds row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32 of the block
-            const int m = (wm * 64) % W2_EROWS + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+            const int m = ii * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
             const int nn = wn * 64 + jj * 32 + (lane & 31);
             tileo[m * W2_BN + 4 * ((nn >> 2) ^ (8 * ((m >> 2) & 1))) + (nn & 3)] = acc[i][jj][vv];
           }
+      }
     }
     __syncthreads();
 #pragma unroll 4
