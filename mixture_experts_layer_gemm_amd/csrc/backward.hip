@@ -403,9 +403,12 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     for (int r = tid >> 5; r < W2_EROWS; r += 8) {
       const int m = m0 + ps * W2_EROWS + r;
       // M and Nc are multiples of 64: a piece is wholly inside or wholly outside
+      // written once and not read back here: non-temporal, so the stream of fp32
+      // gradients does not evict the operand rows from L2
       if (m < pb.M && n < pb.Nc)
-        *reinterpret_cast<floatx4*>(out + static_cast<size_t>(m) * pb.Nc + n) =
-            *reinterpret_cast<const floatx4*>(tileo + r * W2_BN + 4 * (pc ^ (8 * ((r >> 2) & 1))));
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const floatx4*>(tileo + r * W2_BN + 4 * (pc ^ (8 * ((r >> 2) & 1)))),
+            reinterpret_cast<floatx4*>(out + static_cast<size_t>(m) * pb.Nc + n));
     }
   }
 }
