@@ -172,7 +172,8 @@ swiglu_bwd_kernel(int rows, const int32_t* __restrict__ rows_dev, int dff,
 // those reads free of bank conflicts.
 constexpr int W2_BM = 256, W2_BN = 128;       // output tile (M: P columns, N: Q columns)
 constexpr int W2_BK = 32;                     // segment rows per stage
-constexpr int W2_XS = 3;                      // ring depth (stages)
+constexpr int W2_XS = 2;                      // ring depth (stages)
+static_assert(W2_XS == 2 || W2_XS == 3, "the stage waits are written for 2 or 3 stages");
 constexpr int W2_ROWP = W2_BM * 2;            // LDS bytes per stage row of P (256 bf16)
 constexpr int W2_ROWQ = W2_BN * 2;            // LDS bytes per stage row of Q (128 bf16)
 constexpr int W2_OPP = W2_BK * W2_ROWP;       // bytes of P per stage
@@ -180,7 +181,6 @@ constexpr int W2_STAGE = W2_BK * (W2_ROWP + W2_ROWQ);
 constexpr int W2_DPP = W2_OPP / (1024 * 4);   // direct-to-LDS loads of P per wave per stage
 constexpr int W2_DPQ = W2_BK * W2_ROWQ / (1024 * 4);
 constexpr int W2_DPW = W2_DPP + W2_DPQ;       // loads per wave per stage
-constexpr int W2_WAIT = (W2_XS - 2) * W2_DPW; // the later stages may be pending
 constexpr int W2_EROWS = 64;                  // epilogue rows per pass through the ring
 static_assert(W2_XS * W2_STAGE >= W2_EROWS * W2_BN * 4, "the epilogue reuses the ring");
 static_assert(W2_DPP == 4 && W2_DPQ == 2, "each wave loads 8 rows of each operand per stage");
@@ -214,7 +214,7 @@ __device__ __forceinline__ void w2_dma16(uint32_t voff, const void* sbase, uint3
 typedef short w2_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) w2_v4s w2_lv4s;
 
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   __shared__ __attribute__((aligned(1024))) char ring[W2_XS * W2_STAGE];
   typedef __attribute__((address_space(3))) char lds_char;
@@ -336,10 +336,14 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
   for (int v = 0; v < W2_XS - 1; ++v)
     if (v < nst) issue(v, v);
   for (int s = 0; s < nst; ++s) {
-    // this stage's loads have landed (the later stages' may still be in flight)
-    if (s + 2 < nst) wait_vmcnt<W2_WAIT>();
-    else if (s + 1 < nst) wait_vmcnt<W2_DPW>();
-    else wait_vmcnt<0>();
+    // this stage's loads have landed; the stages issued after it (min(XS - 2, nst - 1 - s)
+    // of them: stage s + XS - 2 was issued during stage s - 1) may still be in flight
+    if constexpr (W2_XS == 2) {
+      wait_vmcnt<0>();
+    } else {
+      if (s + 1 < nst) wait_vmcnt<W2_DPW>();
+      else wait_vmcnt<0>();
+    }
     const uint32_t sb = lds0 + (s % W2_XS) * W2_STAGE;
     // rows past the segment (last stage only) read as zero: each wave clears its own rows
     if (j0 + (s + 1) * W2_BK > j1) {
@@ -358,16 +362,17 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     if (s + W2_XS - 1 < nst) issue(s + W2_XS - 1, (s + W2_XS - 1) % W2_XS);
 #pragma unroll
     for (int t = 0; t < W2_BK / 16; ++t) {
-      bf16x8 af[4], bf[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = frag(sb, W2_ROWP, wm * 128 + i * 32, t);
+      // the Q fragments stay, one P fragment at a time (registers for a third workgroup)
+      bf16x8 bf[2];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) bf[jj] = frag(sb + W2_OPP, W2_ROWQ, wn * 64 + jj * 32, t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 af = frag(sb, W2_ROWP, wm * 128 + i * 32, t);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[jj], acc[i][jj], 0, 0, 0);
+      }
     }
   }
   // epilogue through LDS (the ring is free once every wave is past the last stage), in
