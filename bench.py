@@ -94,6 +94,24 @@ def time_eager(torch, fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def time_cold(torch, fn, reps: int, scratch) -> float:
+    """Median GPU time (ms) of single fn() calls, each after a write of `scratch` (larger
+    than the 256 MB Infinity Cache) that leaves neither L2 nor the MALL holding fn's
+    inputs."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(reps):
+        scratch.fill_(i & 0x7F)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
 def cpu_baseline(inp, sample_tokens: int):
     """The oracle as it stands, on the first `sample_tokens` tokens of the workload."""
     import oracle.moe_oracle as O
@@ -231,6 +249,19 @@ def main():
         o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
         reps)
 
+    # the same three stages with cold caches (a 512 MB write before each call)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=x.device)
+    cold = {}
+    cold["route_ms"] = time_cold(torch, lambda: moe.moe_route(
+        x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
+        w_shared_gate=gate, want_counts=False), reps, scratch)
+    cold["permute_ms"] = time_cold(torch, lambda: moe.moe_permute(x, idx, N, cap, copy_rows=False),
+                                   reps, scratch)
+    cold["combine_ms"] = time_cold(torch, lambda: moe.moe_combine(
+        o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
+        reps, scratch)
+    del scratch
+
     # next rows on the same batch: balance statistics, rank-wide capacity (8 destinations
     # of N/8 experts, capacity factor 1), biased selection and the bias controller
     nx = {}
@@ -281,13 +312,14 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic()
-    hbm = {
-        "route": (T * d * esz + N * d * esz + T * K * 8) / (st["route_ms"] * 1e-3) / 1e9,
+    stage_bytes = {
+        "route": T * d * esz + N * d * esz + T * K * 8,
         # count: idx in, ranks out; map: idx + ranks in, dest_row + row_token out
-        "permute": (T * K * 20 + R * 4) / (st["permute_ms"] * 1e-3) / 1e9,
-        "combine": (R * d * esz + (2 if d_s else 1) * T * d * esz + T * K * 8)
-        / (st["combine_ms"] * 1e-3) / 1e9,
+        "permute": T * K * 20 + R * 4,
+        "combine": R * d * esz + (2 if d_s else 1) * T * d * esz + T * K * 8,
     }
+    hbm = {k: b / (st[k + "_ms"] * 1e-3) / 1e9 for k, b in stage_bytes.items()}
+    hbm_cold = {k: b / (cold[k + "_ms"] * 1e-3) / 1e9 for k, b in stage_bytes.items()}
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -318,6 +350,8 @@ def main():
                          mfma_frac=round(flops_gateup / t_gateup / 1e12 / PEAK_BF16_TFLOPS, 4)),
         "stages_ms": {k.replace("_ms", ""): round(v, 4) for k, v in st.items()},
         "stages_hbm_frac": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm.items()},
+        "stages_ms_cold": {k.replace("_ms", ""): round(v, 4) for k, v in cold.items()},
+        "stages_hbm_frac_cold": {k: round(v / PEAK_HBM_GBS, 3) for k, v in hbm_cold.items()},
         "next_rows_ms": {k.replace("_ms", ""): round(v, 4) for k, v in nx.items()},
         "backward_tflops": (round(bwd_flops / (nx["backward_ms"] * 1e-3) / 1e12, 1)
                             if bwd_flops else None),
