@@ -95,14 +95,15 @@ def time_eager(torch, fn, reps: int) -> float:
 
 
 def time_cold(torch, fn, reps: int, scratch) -> float:
-    """Median GPU time (ms) of single fn() calls, each after a write of `scratch` (larger
+    """Median GPU time (ms) of single fn() calls, each after a read of `scratch` (larger
     than the 256 MB Infinity Cache) that leaves neither L2 nor the MALL holding fn's
-    inputs."""
+    inputs. A read, not a write: evicting dirty lines would put write-back traffic inside
+    the timed call."""
     fn()
     torch.cuda.synchronize()
     ts = []
     for i in range(reps):
-        scratch.fill_(i & 0x7F)
+        scratch.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -249,8 +250,8 @@ def main():
         o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
         reps)
 
-    # the same three stages with cold caches (a 512 MB write before each call)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=x.device)
+    # the same three stages with cold caches (a 512 MB read before each call)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=x.device)
     cold = {}
     cold["route_ms"] = time_cold(torch, lambda: moe.moe_route(
         x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,

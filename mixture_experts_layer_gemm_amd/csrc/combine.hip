@@ -4,8 +4,9 @@
 // Capacity, and Load Balancing", Section 10.3).
 //
 // HBM-bound weighted gather: one wave per token, each lane owns 16-byte pieces of the
-// row, the K packed expert rows and the shared row are read once with coalesced
-// 16-byte loads, accumulated in fp32 in slot order, and y is written once.
+// row; the K packed expert rows and the shared row are read once with coalesced
+// 16-byte loads, four slots' loads in flight together, accumulated in fp32 in slot
+// order, and y is written once.
 #include "common.h"
 
 using namespace moe;
@@ -14,12 +15,20 @@ namespace {
 
 constexpr int WAVES = 4;
 
-__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
-  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+constexpr int KG = 4;  // slots whose loads are in flight together
+
+// a 16-byte piece as floats: 8 bf16 or 4 fp32
+template <bool BF16>
+__device__ __forceinline__ void unpack16(const u32x4& u, float* v) {
+  if (BF16) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(u[i] << 16);
-    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
   }
 }
 
@@ -40,37 +49,41 @@ combine_kernel(int T, int d, int K, const void* __restrict__ f_perm,
     rk = topk_r != nullptr ? topk_r[static_cast<size_t>(t) * K + lane] : 1.0f;
   }
   const float st = (s_tok != nullptr) ? s_tok[t] : s;
+  const char* fb = static_cast<const char*>(f_perm);
+  const char* gb = static_cast<const char*>(g);
+  const size_t rowb = static_cast<size_t>(d) * (BF16 ? 2 : 4);
   const int npc = d / EPP;
   for (int j = lane; j < npc; j += kWave) {
     float acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int row = __shfl(dk, k, kWave);
-      const float rr = __shfl(rk, k, kWave);
-      if (row < 0) continue;
-      float v[EPP];
-      if (BF16) {
-        load8(static_cast<const uint16_t*>(f_perm) + static_cast<size_t>(row) * d + j * EPP, v);
-      } else {
-        const floatx4 u = *reinterpret_cast<const floatx4*>(
-            static_cast<const float*>(f_perm) + static_cast<size_t>(row) * d + j * EPP);
+    // slots in groups of KG: the group's loads (and the shared row's, with the first
+    // group) are all issued before the first is used; accumulation stays in slot order
+    u32x4 gv = u32x4{0u, 0u, 0u, 0u};
+    if (g != nullptr) gv = *reinterpret_cast<const u32x4*>(gb + static_cast<size_t>(t) * rowb + j * 16);
+    for (int k0 = 0; k0 < K; k0 += KG) {
+      int row[KG];
+      float rr[KG];
+      u32x4 fv[KG];
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) v[e] = u[e];
+      for (int q = 0; q < KG; ++q) {
+        row[q] = k0 + q < K ? __shfl(dk, k0 + q, kWave) : -1;
+        rr[q] = __shfl(rk, min(k0 + q, K - 1), kWave);
+        if (row[q] >= 0)
+          fv[q] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(row[q]) * rowb + j * 16);
       }
 #pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[e] = fmaf(rr, v[e], acc[e]);
+      for (int q = 0; q < KG; ++q) {
+        if (row[q] < 0) continue;
+        float v[EPP];
+        unpack16<BF16>(fv[q], v);
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) acc[e] = fmaf(rr[q], v[e], acc[e]);
+      }
     }
     if (g != nullptr) {
       float v[EPP];
-      if (BF16) {
-        load8(static_cast<const uint16_t*>(g) + static_cast<size_t>(t) * d + j * EPP, v);
-      } else {
-        const floatx4 u = *reinterpret_cast<const floatx4*>(
-            static_cast<const float*>(g) + static_cast<size_t>(t) * d + j * EPP);
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) v[e] = u[e];
-      }
+      unpack16<BF16>(gv, v);
 #pragma unroll
       for (int e = 0; e < EPP; ++e) acc[e] = fmaf(st, v[e], acc[e]);
     }
