@@ -21,7 +21,7 @@ def kernel_bodies(asm: str, name_part: str) -> dict:
     out = {}
     for m in re.finditer(r"^(_Z\S*" + re.escape(name_part) + r"\S*):", asm, flags=re.M):
         start = m.end()
-        end = asm.find("s_endpgm", start)
+        end = asm.find(".Lfunc_end", start)  # a kernel may hold several s_endpgm (early exits)
         out[m.group(1)] = asm[start:end]
     return out
 
