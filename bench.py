@@ -359,6 +359,12 @@ def main():
         "next_rows_hbm_frac": {"balance_stats": round(
             nx_bytes["balance_stats"] / (nx["balance_stats_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
     }
+    # what a plain streaming read reaches on this GPU (row sums over 1 GiB of fp32 that no
+    # cache holds), the practical ceiling beside the 8 TB/s spec figure
+    probe = torch.ones(256 << 20, dtype=torch.float32, device=x.device).view(-1, 4096)
+    probe_ms = time_eager(torch, lambda: probe.sum(dim=1), 5)
+    out["hbm_read_probe_gbs"] = round(probe.numel() * 4 / (probe_ms * 1e-3) / 1e9, 1)
+    del probe
     torch.cuda.synchronize()
     if args.copy_probe_mib > 0:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=x.device)
