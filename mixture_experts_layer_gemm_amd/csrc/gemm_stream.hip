@@ -27,6 +27,7 @@
 // Wave w of a tile owns weight blocks (32 rows each) w * NBW .. w * NBW + NBW - 1 of the
 // tile's 128 NBW weight rows (SwiGLU: NBW / 2 gate blocks and the matching up blocks)
 // and all BM = 32 XBM activation rows.
+#include <atomic>
 #include <utility>
 
 #include "gemm_common.h"
@@ -541,16 +542,17 @@ static bool supported(int mode, const StreamProblem& p0, const StreamProblem& p1
 static hipError_t launch(int mode, const StreamProblem& p0, const StreamProblem& p1,
                          hipStream_t stream) {
   if (!supported(mode, p0, p1)) return hipErrorNotSupported;
-  static int cus[64] = {0};
+  // compute units per device, looked up once (host threads may race to store the same value)
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  int n_cu = cus[dev].load(std::memory_order_relaxed);
+  if (n_cu == 0) {
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
-    cus[dev] = n;
+    cus[dev].store(n_cu, std::memory_order_relaxed);
   }
-  const int grid = cus[dev] / 8 * 8;
+  const int grid = n_cu / 8 * 8;
   if (grid <= 0) return hipErrorNotSupported;
   if (mode == SK_SWIGLU)
     hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_SWIGLU>), dim3(grid),
