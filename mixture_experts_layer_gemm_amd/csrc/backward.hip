@@ -181,9 +181,12 @@ constexpr int W2_STAGE = W2_BK * (W2_ROWP + W2_ROWQ);
 constexpr int W2_DPP = W2_OPP / (1024 * 4);   // direct-to-LDS loads of P per wave per stage
 constexpr int W2_DPQ = W2_BK * W2_ROWQ / (1024 * 4);
 constexpr int W2_DPW = W2_DPP + W2_DPQ;       // loads per wave per stage
+constexpr int W2_RPP = 1024 / W2_ROWP;        // P rows per load
+constexpr int W2_CPP = W2_ROWP / 16;          // 16-byte chunks per P row
+constexpr int W2_PB = W2_BM / 64;             // 32-column P blocks per wave (half the tile)
 constexpr int W2_EROWS = 64;                  // epilogue rows per pass through the ring
 static_assert(W2_XS * W2_STAGE >= W2_EROWS * W2_BN * 4, "the epilogue reuses the ring");
-static_assert(W2_DPP == 4 && W2_DPQ == 2, "each wave loads 8 rows of each operand per stage");
+static_assert(W2_DPP * W2_RPP == 8 && W2_DPQ == 2, "each wave loads 8 rows of each operand per stage");
 
 struct WgradProblem {
   const uint16_t* P;      // [rows][ldp], columns [0, M) used
@@ -268,12 +271,12 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     const uint32_t sb = lds0 + slot * W2_STAGE;
 #pragma unroll
     for (int i = 0; i < W2_DPP; ++i) {
-      const int row = rb + 2 * i + (lane >> 5);
-      const int grow = min(jr + 2 * i + (lane >> 5), j1 - 1);
-      int col = m0 + 8 * w2_swz(row, lane & 31);
+      const int row = rb + W2_RPP * i + lane / W2_CPP;
+      const int grow = min(jr + W2_RPP * i + lane / W2_CPP, j1 - 1);
+      int col = m0 + 8 * w2_swz(row, lane % W2_CPP);
       if (col >= pb.M) col = 0;
       const uint32_t off = static_cast<uint32_t>((static_cast<long>(grow) * pb.ldp + col) * 2);
-      w2_dma16(off, pb.P, sb + (rb + 2 * i) * W2_ROWP);
+      w2_dma16(off, pb.P, sb + (rb + W2_RPP * i) * W2_ROWP);
     }
 #pragma unroll
     for (int i = 0; i < W2_DPQ; ++i) {
@@ -322,11 +325,11 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
     return __builtin_bit_cast(bf16x8, both);
   };
 
-  // wave (wm, wn) owns tile rows wm * 128 .. + 127 (4 blocks of 32) and columns
-  // wn * 64 .. + 63 (2 blocks of 32)
-  floatx16 acc[4][2];
+  // wave (wm, wn) owns tile rows wm * BM / 2 .. + BM / 2 - 1 (PB blocks of 32) and
+  // columns wn * 64 .. + 63 (2 blocks of 32)
+  floatx16 acc[W2_PB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < W2_PB; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -350,10 +353,10 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
       const int r = rb + (lane >> 3);
       if (j0 + s * W2_BK + r >= j1) {
         typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-        lds_u32x4* zp = (lds_u32x4*)((lds_char*)nullptr + sb + r * W2_ROWP + (lane & 7) * 64);
+        lds_u32x4* zp = (lds_u32x4*)((lds_char*)nullptr + sb + r * W2_ROWP + (lane & 7) * (W2_ROWP / 8));
         lds_u32x4* zq = (lds_u32x4*)((lds_char*)nullptr + sb + W2_OPP + r * W2_ROWQ + (lane & 7) * 32);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) zp[c] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < W2_ROWP / 128; ++c) zp[c] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int c = 0; c < 2; ++c) zq[c] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -367,8 +370,8 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) bf[jj] = frag(sb + W2_OPP, W2_ROWQ, wn * 64 + jj * 32, t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 af = frag(sb, W2_ROWP, wm * 128 + i * 32, t);
+      for (int i = 0; i < W2_PB; ++i) {
+        const bf16x8 af = frag(sb, W2_ROWP, wm * (W2_BM / 2) + i * 32, t);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[jj], acc[i][jj], 0, 0, 0);
@@ -386,18 +389,18 @@ wgrad_kernel(WgradProblem q0, WgradProblem q1, int s_per, int r_per) {
 #pragma unroll
   for (int ps = 0; ps < W2_BM / W2_EROWS; ++ps) {
     __syncthreads();
-    // pass ps holds tile rows 64 ps .. + 63: blocks i = 2 (ps & 1) + {0, 1} of the waves
-    // with wm = ps / 2
-    if (wm == ps / 2) {
+    // pass ps holds tile rows 64 ps .. + 63: the waves' 32-row blocks wm PB + i with
+    // (wm PB + i) / 2 = ps
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * (ps & 1) + ii;
+    for (int i = 0; i < W2_PB; ++i) {
+      const int gb = wm * W2_PB + i;
+      if (gb / 2 == ps) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int vv = 0; vv < 16; ++vv) {
             // lane holds row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32 of the block
-            const int m = ii * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+            const int m = (gb & 1) * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
             const int nn = wn * 64 + jj * 32 + (lane & 31);
             tileo[m * W2_BN + 4 * ((nn >> 2) ^ (8 * ((m >> 2) & 1))) + (nn & 3)] = acc[i][jj][vv];
           }
