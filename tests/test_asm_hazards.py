@@ -2,6 +2,7 @@
 awaits them with one explicit vmcnt wait per stage; compile it and check the generated
 gfx950 code keeps that contract (no use or copy of an in-flight register, no scratch)."""
 import os
+import re
 import shutil
 
 import pytest
@@ -24,3 +25,23 @@ def test_persistent_gemm_has_no_untracked_load_hazard(tmp_path):
         assert not hz, f"{name}: {hz[:3]}"
         # one explicit wait per stage of the 4-stage unrolled loop, plus entry/exit drains
         assert body.count("s_waitcnt vmcnt(32)") == 4, name
+
+
+@pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None, reason="hipcc not installed")
+@pytest.mark.parametrize("src", ["gemm_stream.hip", "gemm.hip", "gemm_packed.hip", "backward.hip"])
+def test_m0_is_only_set_for_direct_to_lds_loads(src, tmp_path):
+    """The direct-to-LDS loads set M0 in inline asm and list it as clobbered. M0 is a
+    reserved register the compiler does not preserve around such asm, so that is only
+    safe while the compiler itself never uses M0 in these kernels: every instruction
+    that names m0 must be one of the asm statements' own s_mov_b32 m0, s<n>."""
+    asm = compile_to_asm(os.path.join(CSRC, src), os.path.join(ROOT, "include"),
+                         str(tmp_path / (src + ".s")))
+    bad = []
+    for line in asm.split("\n"):
+        t = line.strip()
+        if not t or t.startswith(";") or t.startswith("."):
+            continue
+        code = t.split(";")[0]
+        if re.search(r"\bm0\b", code) and not re.match(r"s_mov_b32 m0, s\d+$", code.strip()):
+            bad.append(t)
+    assert not bad, bad[:5]
