@@ -37,7 +37,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int SK_THREADS = 256;
+constexpr int SK_GT = 256;           // threads that build the group tables (<= 256 groups)
 constexpr int SK_BKX = 64;           // k per stage
 constexpr int SK_XS = 4;             // activation ring depth (stages)
 constexpr int SK_SPS = SK_BKX / 16;  // k16 steps per stage
@@ -76,13 +76,18 @@ __device__ __forceinline__ void sk_unroll(F&& f) {
   sk_unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int NBW, int XBM, int RS>
+// RH row halves: wave v takes weight position v % 4 and tile rows (v / 4) * 32 XBM ..
+// + 32 XBM - 1; the waves of one position load the same weight blocks
+template <int NBW, int XBM, int RS, int RH>
 struct SK {
-  static constexpr int BM = 32 * XBM;
+  static constexpr int WAVES = 4 * RH;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int HROWS = 32 * XBM;            // rows per row half
+  static constexpr int BM = HROWS * RH;             // rows per tile
   static constexpr int COLS_SWIGLU = 64 * NBW;   // output columns of a SwiGLU tile
   static constexpr int COLS_PLAIN = 128 * NBW;
   static constexpr int XSTAGE = BM * SK_BKX * 2;  // bytes
-  static constexpr int XDPW = XSTAGE / 4096;      // direct-to-LDS loads per wave per stage
+  static constexpr int XDPW = XSTAGE / (1024 * WAVES);  // direct-to-LDS loads per wave per stage
   static constexpr int WPS = SK_SPS * NBW;        // weight loads per wave per stage
   static constexpr int PER = XDPW + WPS;          // vector memory ops per wave per stage
   // ops issued after the weights (resp. activations) of stage s when stage s begins
@@ -90,7 +95,7 @@ struct SK {
   static constexpr int AFTER_X = WPS + (SK_XS - 2) * PER;
   static constexpr int WAITN = AFTER_W < AFTER_X ? AFTER_W : AFTER_X;
   static_assert(WAITN <= 63, "vmcnt range");
-  static_assert(XDPW * 4096 == XSTAGE, "whole direct-to-LDS loads per stage");
+  static_assert(XDPW * 1024 * WAVES == XSTAGE, "whole direct-to-LDS loads per stage");
   static_assert(BM <= 256, "row index buffer");
 };
 
@@ -108,15 +113,15 @@ struct SkTile {
 // epilogue takes dH and writes H = SiLU(A) B and [dA | dB] instead of SiLU(A) B alone)
 constexpr int SK_PLAIN = 0, SK_SWIGLU = 1, SK_SWIGLU_BWD = 2;
 
-template <int NBW, int XBM, int RS, int MODE>
-__global__ void __launch_bounds__(SK_THREADS, 1)
+template <int NBW, int XBM, int RS, int RH, int MODE>
+__global__ void __launch_bounds__(64 * 4 * RH, 1)
 gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
-  using C = SK<NBW, XBM, RS>;
+  using C = SK<NBW, XBM, RS, RH>;
   constexpr bool SWIGLU = MODE != SK_PLAIN;
   constexpr int COLS = SWIGLU ? C::COLS_SWIGLU : C::COLS_PLAIN;
   __shared__ int s_off[kMaxN + 2];     // packed row offsets of the groups (p1 last)
-  __shared__ int s_tstart[SK_THREADS + 1];
-  __shared__ int s_cstart[SK_THREADS + 1];
+  __shared__ int s_tstart[SK_GT + 1];
+  __shared__ int s_cstart[SK_GT + 1];
   __shared__ int s_rows[2][256];       // gathered activation rows of the current / next tile
   __shared__ __attribute__((aligned(1024))) char lds[SK_XS * C::XSTAGE];
   // SwiGLU backward: the tile's dH rows ([BM][COLS] bf16, 16-byte chunks of row r permuted
@@ -131,12 +136,12 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   // ---- tile list: per-group tile counts and costs, prefix-summed in LDS ----
   // cost of a tile = active 32-row blocks x k stages; a group's tiles cost
   // n-tiles x ceil(rows / 32) x stages in all
-  for (int g = tid; g <= G0; g += SK_THREADS)
+  for (int g = tid; g <= G0; g += C::THREADS)
     s_off[g] = (p0.offsets != nullptr) ? p0.offsets[g] : (g == 0 ? 0 : p0.rows);
   __syncthreads();
   if (tid == 0) s_off[G0 + 1] = s_off[G0] + p1.rows;
   __syncthreads();
-  {
+  if (tid < SK_GT) {
     int cnt = 0, cost = 0;
     if (tid < NG) {
       const StreamProblem& P = tid < G0 ? p0 : p1;
@@ -152,12 +157,15 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     s_cstart[0] = 0;
   }
   __syncthreads();
-  for (int off = 1; off < SK_THREADS; off <<= 1) {  // inclusive scans over <= 256 groups
-    const int v = (tid >= off) ? s_tstart[tid + 1 - off] : 0;
-    const int c = (tid >= off) ? s_cstart[tid + 1 - off] : 0;
+  for (int off = 1; off < SK_GT; off <<= 1) {  // inclusive scans over <= 256 groups
+    const bool gt = tid < SK_GT;
+    const int v = (gt && tid >= off) ? s_tstart[tid + 1 - off] : 0;
+    const int c = (gt && tid >= off) ? s_cstart[tid + 1 - off] : 0;
     __syncthreads();
-    s_tstart[tid + 1] += v;
-    s_cstart[tid + 1] += c;
+    if (gt) {
+      s_tstart[tid + 1] += v;
+      s_cstart[tid + 1] += c;
+    }
     __syncthreads();
   }
   const int total = s_tstart[NG];
@@ -178,7 +186,7 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     const long u = (target - s_cstart[lo] + nst - 1) / nst;  // 32-row blocks into the group
     int nt = static_cast<int>(u / rb);
     const int rem = static_cast<int>(u - static_cast<long>(nt) * rb);
-    int mt = ceil_div(rem, XBM);
+    int mt = ceil_div(rem, C::BM / 32);
     if (mt >= mtiles) {
       ++nt;
       mt = 0;
@@ -194,7 +202,9 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   if (t >= t_end) return;
 
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave
+  const int w = wv & 3;                                    // weight position
+  const int rh = wv >> 2;                                  // row half
   const uint32_t lds_base = static_cast<uint32_t>((size_t)((lds_char*)lds));
   const uint32_t rows_base = static_cast<uint32_t>((size_t)((lds_char*)(&s_rows[0][0])));
   const uint32_t dh_base = static_cast<uint32_t>((size_t)((lds_char*)dhbuf));
@@ -238,14 +248,14 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     return reinterpret_cast<const char*>(base + static_cast<size_t>(nb) * 32 * P.Kd);
   };
   // packed row (within the tile) behind this lane's DMA slot i
-  auto slot_row = [&](int i) -> int { return ((4 * i + w) * 64 + lane) >> 3; };
+  auto slot_row = [&](int i) -> int { return ((C::WAVES * i + wv) * 64 + lane) >> 3; };
   // direct-to-LDS copy of tile k's gathered activation rows into row buffer `slot`
   // (rows past the tile repeat its last row)
   auto fetch_rows = [&](const SkTile& k, int slot) {
     const StreamProblem& P = prob(k);
-    if (P.row_index != nullptr) {
-      const int r = k.row0 + min(w * 64 + lane, k.rows - 1);
-      sk_dma4(static_cast<uint32_t>(r) * 4u, P.row_index, rows_base + slot * 1024 + w * 256);
+    if (P.row_index != nullptr && wv * 64 < C::BM) {
+      const int r = k.row0 + min(wv * 64 + lane, k.rows - 1);
+      sk_dma4(static_cast<uint32_t>(r) * 4u, P.row_index, rows_base + slot * 1024 + wv * 256);
     }
   };
   // activation row of each of this lane's DMA slots for tile k
@@ -260,13 +270,13 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   auto issue_x = [&](const SkTile& k, const uint32_t* xr, int ks, int ring_slot) {
     const StreamProblem& P = prob(k);
     const uint32_t kbytes = static_cast<uint32_t>(P.Kd) * 2u;
-    const uint32_t dst = lds_base + ring_slot * C::XSTAGE + w * 1024;
+    const uint32_t dst = lds_base + ring_slot * C::XSTAGE + wv * 1024;
 #pragma unroll
     for (int i = 0; i < C::XDPW; ++i) {
-      const int s = (4 * i + w) * 64 + lane;
+      const int s = (C::WAVES * i + wv) * 64 + lane;
       const uint32_t off = xr[i] * kbytes +
                            static_cast<uint32_t>(sk_swz(s >> 3, s & 7) * 16 + ks * (SK_BKX * 2));
-      sk_dma16(off, P.a, dst + i * 4096);
+      sk_dma16(off, P.a, dst + i * (1024 * C::WAVES));
     }
   };
 
@@ -327,7 +337,9 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     fetch_rows(nxt, kslot ^ 1);  // published by the stage barriers before its first use
     const bool has_nn = t + 2 * step < t_end;
     const SkTile nn = has_nn ? tile_at(t + 2 * step) : nxt;
-    const int xb = __builtin_amdgcn_readfirstlane(ceil_div(cur.rows, 32));
+    // 32-row blocks of this wave's row half that hold rows of the tile
+    const int xb = __builtin_amdgcn_readfirstlane(
+        min(XBM, max(0, ceil_div(cur.rows - rh * C::HROWS, 32))));
     const int nst = cur.nst;
 
     floatx16 acc[NBW][XBM];
@@ -371,17 +383,21 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
           const int kc = 2 * u + lh;
 #pragma unroll
           for (int j = 0; j < XBM; ++j) {
-            const int row = 32 * j + lr;
+            const int row = rh * C::HROWS + 32 * j + lr;
             xv[j] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4*>(xs + row * (SK_BKX * 2) + (sk_swz(row, kc) << 4)));
           }
         };
-        bf16x8 xv[2][XBM];
-        xread(0, xv[0]);
+        // double-buffered activation fragments with one row half; with two (half the
+        // registers per wave) one set at a time
+        constexpr int XV = RH == 1 ? 2 : 1;
+        bf16x8 xv[XV][XBM];
+        if (XV == 2) xread(0, xv[0]);
 #pragma unroll
         for (int u = 0; u < SK_SPS; ++u) {
-          const int cb = u & 1;
-          if (u + 1 < SK_SPS) xread(u + 1, xv[cb ^ 1]);
+          const int cb = XV == 2 ? (u & 1) : 0;
+          if (XV == 2 && u + 1 < SK_SPS) xread(u + 1, xv[cb ^ 1]);
+          if (XV == 1) xread(u, xv[0]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < XBM; ++j) {
@@ -433,7 +449,7 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
 #pragma unroll
       for (int j = 0; j < XBM; ++j) {
         if (j >= xb) break;
-        const int m = 32 * j + lr;
+        const int m = rh * C::HROWS + 32 * j + lr;
         const bool ok = m < cur.rows;
         const size_t prow = static_cast<size_t>(cur.row0 + (ok ? m : 0));
         uint16_t* orow = P.out + prow * P.Nd;
@@ -476,17 +492,31 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
             put(pa, abrow, ok);
             put(pb, abrow + P.Nd, ok);
           } else {
-            u32x2 pk[4];
+            // two halves of the block (columns 0..15, 16..31), one exchange each, so that
+            // only half a block's packed values are live at a time
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float h[4];
+            for (int hf = 0; hf < 2; ++hf) {
+              u32x2 pk[2];
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                h[e] = SWIGLU ? silu_f(acc[ob][j][4 * q + e]) * acc[ob + NBW / 2][j][4 * q + e]
-                              : acc[ob][j][4 * q + e];
-              pk[q] = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+              for (int qq = 0; qq < 2; ++qq) {
+                const int q = 2 * hf + qq;
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  h[e] = SWIGLU ? silu_f(acc[ob][j][4 * q + e]) * acc[ob + NBW / 2][j][4 * q + e]
+                                : acc[ob][j][4 * q + e];
+                pk[qq] = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+              }
+              // lh = 0 keeps q = 2 hf and receives the partner's; lh = 1 keeps q = 2 hf + 1
+              const u32x2 sv = lh ? pk[0] : pk[1];
+              u32x2 rv;
+              rv[0] = __shfl_xor(sv[0], 32, kWave);
+              rv[1] = __shfl_xor(sv[1], 32, kWave);
+              const u32x4 c = lh ? u32x4{rv[0], rv[1], pk[1][0], pk[1][1]}
+                                 : u32x4{pk[0][0], pk[0][1], rv[0], rv[1]};
+              if (ok) *reinterpret_cast<u32x4*>(orow + n + 16 * hf + 8 * lh) = c;
+              __builtin_amdgcn_sched_barrier(0);
             }
-            put(pk, orow + n, ok);
           }
           __builtin_amdgcn_sched_barrier(0);  // one block's values live at a time
         }
@@ -509,14 +539,17 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   wait_vmcnt<0>();  // no direct-to-LDS load may land after the workgroup ends
 }
 
-// tile shape: 2 weight blocks per wave, 128 rows, 4 stages of weights in flight
-constexpr int kNBW = 2, kXBM = 4, kRS = 4;
+// tile shapes: 2 weight blocks per wave, 128 rows per row half. One row half (4 waves)
+// with 4 stages of weights in flight; for few experts with many rows each (at least
+// kRowsRH2 per group), two row halves (8 waves, 2 waves per SIMD, so 2 stages of weights
+// in flight) that share every weight block fetched into the CU.
+constexpr int kNBW = 2, kXBM = 4, kRS = 4, kRS2 = 2, kRowsRH2 = 1024;
 
 bool fits(int mode, const StreamProblem& P) {
   const bool swiglu = mode != SK_PLAIN;
   if (P.rows <= 0) return true;
   if (mode == SK_SWIGLU_BWD && (P.dh == nullptr || P.dab == nullptr)) return false;
-  using C = SK<kNBW, kXBM, kRS>;
+  using C = SK<kNBW, kXBM, kRS, 1>;  // both row-half shapes share COLS and the stage rule
   const int cols = swiglu ? C::COLS_SWIGLU : C::COLS_PLAIN;
   const int nst = P.Kd / SK_BKX;
   if (P.G <= 0 || P.G > kMaxN || P.a == nullptr || P.w0 == nullptr || P.out == nullptr)
@@ -535,7 +568,7 @@ bool fits(int mode, const StreamProblem& P) {
 
 static bool supported(int mode, const StreamProblem& p0, const StreamProblem& p1) {
   if (p0.rows <= 0 || !fits(mode, p0) || !fits(mode, p1)) return false;
-  if (p1.rows > 0 && (p1.offsets != nullptr || p1.G != 1 || p0.G + 1 > SK_THREADS)) return false;
+  if (p1.rows > 0 && (p1.offsets != nullptr || p1.G != 1 || p0.G + 1 > SK_GT)) return false;
   return true;
 }
 
@@ -554,15 +587,23 @@ static hipError_t launch(int mode, const StreamProblem& p0, const StreamProblem&
   }
   const int grid = n_cu / 8 * 8;
   if (grid <= 0) return hipErrorNotSupported;
-  if (mode == SK_SWIGLU)
-    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_SWIGLU>), dim3(grid),
-                       dim3(SK_THREADS), 0, stream, p0, p1);
+  const bool rh2 = mode != SK_SWIGLU_BWD && p0.rows >= static_cast<long>(kRowsRH2) * p0.G;
+  const dim3 block(rh2 ? 512 : 256);
+  if (mode == SK_SWIGLU && rh2)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS2, 2, SK_SWIGLU>), dim3(grid), block,
+                       0, stream, p0, p1);
+  else if (mode == SK_SWIGLU)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, 1, SK_SWIGLU>), dim3(grid), block,
+                       0, stream, p0, p1);
   else if (mode == SK_SWIGLU_BWD)
-    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_SWIGLU_BWD>), dim3(grid),
-                       dim3(SK_THREADS), 0, stream, p0, p1);
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, 1, SK_SWIGLU_BWD>), dim3(grid),
+                       block, 0, stream, p0, p1);
+  else if (rh2)
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS2, 2, SK_PLAIN>), dim3(grid), block,
+                       0, stream, p0, p1);
   else
-    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, SK_PLAIN>), dim3(grid),
-                       dim3(SK_THREADS), 0, stream, p0, p1);
+    hipLaunchKernelGGL((gemm_stream_kernel<kNBW, kXBM, kRS, 1, SK_PLAIN>), dim3(grid), block,
+                       0, stream, p0, p1);
   return hipGetLastError();
 }
 

@@ -18,13 +18,24 @@ def test_persistent_gemm_has_no_untracked_load_hazard(tmp_path):
     asm = compile_to_asm(os.path.join(CSRC, "gemm_stream.hip"), os.path.join(ROOT, "include"),
                          str(tmp_path / "gemm_stream.s"))
     bodies = kernel_bodies(asm, "gemm_stream_kernel")
-    assert len(bodies) == 3, sorted(bodies)  # plain, SwiGLU and SwiGLU-backward instantiations
+    # one row half: plain, SwiGLU, SwiGLU backward; two row halves: plain, SwiGLU
+    assert len(bodies) == 5, sorted(bodies)
     for name, body in bodies.items():
-        assert "scratch_" not in body, f"{name} spills to scratch"
+        nbw, xbm, rs, rh, mode = (int(v) for v in re.findall(r"Li(\d+)E", name)[:5])
+        # the two-row-half shape has half the registers per wave and spills a few loop
+        # invariants; scratch operations only add to the in-order vector-memory count, so
+        # they can only make the explicit waits stricter (the hazard below is a copy or
+        # spill of a register an untracked load has not filled yet)
+        if rh == 1:
+            assert "scratch_" not in body, f"{name} spills to scratch"
         hz = untracked_load_hazards(body)
         assert not hz, f"{name}: {hz[:3]}"
-        # one explicit wait per stage of the 4-stage unrolled loop, plus entry/exit drains
-        assert body.count("s_waitcnt vmcnt(32)") == 4, name
+        # one explicit wait per stage of the RS-stage unrolled loop, with the count the
+        # stage's later loads allow: PER ops per stage (activation loads XBM, weight loads
+        # 4 NBW), the weights RS - 1 stages ahead, the activations 3 stages ahead
+        per = xbm + 4 * nbw
+        waitn = min((rs - 1) * per, 4 * nbw + 2 * per)
+        assert body.count(f"s_waitcnt vmcnt({waitn})") == rs, (name, waitn)
 
 
 @pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None, reason="hipcc not installed")
