@@ -344,7 +344,7 @@ def main():
         "expert_gemm_tflops": round(expert_tflops, 1),
         "expert_gemm_frac_bf16_peak": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": dict(kernel="gate/up pass: routed experts (gathered rows) + shared MLP, "
-                         "SwiGLU fused (gemm_stream_kernel<2,4,4,1>)" if pk else
+                         "SwiGLU fused (gemm_stream_kernel<2,4,4,1,1>)" if pk else
                          "routed gate/up grouped GEMM (row-major weights)",
                          **roof, algorithmic_bytes=bytes_gateup, flops_per_launch=flops_gateup,
                          mfma_tflops=round(flops_gateup / t_gateup / 1e12, 1),
