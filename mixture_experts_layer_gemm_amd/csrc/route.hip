@@ -12,7 +12,10 @@
 // streamed once; W_r stays in L2), and the per-wave partial tiles summed in LDS in a
 // fixed order. Phase 2 gives each wave BT / waves tokens: top-K by ranks of packed
 // (ordered float key, inverted expert index) 64-bit values, which put the lowest index
-// first on ties, then the coefficients in the lanes k < K.
+// first on ties, then the coefficients in the lanes k < K. For N > 64 (several keys per
+// lane) the ranks are counted only among the keys at or above a threshold: the K-th
+// largest of the 64 per-lane maxima. K distinct keys reach it, so the K largest keys all
+// do, and at most K lanes, hence K * N / 64 keys, can hold keys that reach it.
 //
 // Auxiliary-loss-free balancing ("Section 10: Routing, Capacity, and Load Balancing",
 // Eq. 35): with a persistent expert bias b the keys become z + b (softmax rules) or
@@ -54,6 +57,59 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// orders this wave's LDS writes before its later LDS reads (lanes of one wave only)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes the experts of the K largest packed keys to sel[0..K-1], largest first. Lane l
+// holds the keys of experts l + 64 j in mine[j] (0 where l + 64 j >= N; every valid key
+// is nonzero and all valid keys are distinct). key is this wave's LDS scratch of kMaxN
+// entries; sel is read back after a wave_lds_sync().
+__device__ __forceinline__ void select_topk(const uint64_t (&mine)[kMaxN / kWave], int N, int K,
+                                            int lane, uint64_t* key, int* sel) {
+  if (N <= kWave) {  // one key per lane: rank among all N
+    key[lane] = mine[0];
+    wave_lds_sync();
+    int rank = 0;
+#pragma unroll 8
+    for (int i = 0; i < N; ++i) rank += key[i] > mine[0] ? 1 : 0;  // broadcast reads
+    if (lane < N && rank < K) sel[rank] = lane;
+    return;
+  }
+  // threshold: the K-th largest of the per-lane maxima (every lane holds a valid key)
+  uint64_t lmax = mine[0];
+#pragma unroll
+  for (int j = 1; j < kMaxN / kWave; ++j) lmax = mine[j] > lmax ? mine[j] : lmax;
+  key[lane] = lmax;
+  wave_lds_sync();
+  int r = 0;
+#pragma unroll 8
+  for (int i = 0; i < kWave; ++i) r += key[i] > lmax ? 1 : 0;
+  if (r == K - 1) key[kWave] = lmax;  // slot 64: read by no lane above
+  wave_lds_sync();
+  const uint64_t theta = key[kWave];
+  // candidates (keys >= theta, at most K * (kMaxN / 64) <= 64) packed into slots 128..
+  uint64_t* cand = key + 2 * kWave;
+  int nc = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxN / kWave; ++j) {
+    const bool c = mine[j] >= theta;
+    const uint64_t b = __ballot(c);
+    if (c) cand[nc + __popcll(b & ((1ull << lane) - 1ull))] = mine[j];
+    nc += __popcll(b);
+  }
+  wave_lds_sync();
+  if (lane < nc) {
+    const uint64_t mk = cand[lane];
+    int rank = 0;
+    for (int i = 0; i < nc; ++i) rank += cand[i] > mk ? 1 : 0;
+    if (rank < K) sel[rank] = static_cast<int>(~static_cast<uint32_t>(mk));
+  }
+}
 
 // ---- phase 1, bf16: MFMA logits into part[w][BT][ldz] -----------------------------
 // Wave w owns the 32-wide k steps w, w + WAVES, ...; U steps at a time it first issues
@@ -204,10 +260,10 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
 
   // ---- phase 2: top-K and coefficients, one wave per token --------------------------
-  // Selection by rank: every expert's packed key goes to LDS, each lane counts the keys
-  // above each of its own (all comparisons independent, no cross-lane chains), and the
-  // expert of rank k < K lands in slot k. Equal float keys are ordered by the packed
-  // inverted index, so the lower index ranks first.
+  // Selection by rank (select_topk): packed keys go to LDS, each lane counts the keys
+  // above its own (all comparisons independent, no cross-lane chains), and the expert of
+  // rank k < K lands in slot k. Equal float keys are ordered by the packed inverted
+  // index, so the lower index ranks first.
   const int lane = tid & 63;
   const int w = tid >> 6;
   const bool biased = sel_bias != nullptr;
@@ -233,25 +289,10 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
         if (biased) key = (score == 1 ? sigmoid_f(key) : key) + bias_r[j];
         mine[j] = (static_cast<uint64_t>(ord_key(key)) << 32) |
                   static_cast<uint64_t>(~static_cast<uint32_t>(e));
-        s_key[w][e] = mine[j];
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int j = 0; j < kMaxN / kWave; ++j) {
-      if (j * kWave >= N) break;  // uniform
-      int rank = 0;
-#pragma unroll 8
-      for (int i = 0; i < N; ++i)
-        rank += s_key[w][i] > mine[j] ? 1 : 0;  // one address for all lanes: a broadcast
-      const int e = lane + j * kWave;
-      if (e < N && rank < K) s_sel[w][rank] = e;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    select_topk(mine, N, K, lane, s_key[w], s_sel[w]);
+    wave_lds_sync();
     const int sele = lane < K ? s_sel[w][lane] : 0;
     const float selz = lane < K ? zr[sele] : 0.f;
     const bool act = lane < K;

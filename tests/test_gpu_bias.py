@@ -47,7 +47,7 @@ def check_selection(idx_gpu, z32, b32, score, K):
     return len(bad)
 
 
-@pytest.mark.parametrize("N,K", [(8, 2), (64, 4), (256, 8), (16, 16), (5, 3)])
+@pytest.mark.parametrize("N,K", [(8, 2), (64, 4), (256, 8), (16, 16), (5, 3), (65, 16), (200, 7)])
 @pytest.mark.parametrize("score,renorm", [(0, 1), (0, 0), (1, 1), (2, 1)])
 def test_biased_topk_on_identical_logits(N, K, score, renorm):
     say(f"biased topk N={N} K={K} score={score} renorm={renorm}")

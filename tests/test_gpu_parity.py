@@ -43,7 +43,8 @@ def layer(name) -> DeviceLayer:
 # ---------------------------------------------------------------------------------------
 # a2: top-K and coefficients on identical fp32 logits
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("N,K", [(8, 2), (64, 4), (256, 8), (16, 16), (5, 3), (1, 1), (200, 7)])
+@pytest.mark.parametrize("N,K", [(8, 2), (64, 4), (256, 8), (16, 16), (5, 3), (1, 1), (200, 7),
+                                 (65, 16), (256, 16), (130, 1), (128, 5)])
 @pytest.mark.parametrize("score,renorm", [(0, 1), (0, 0), (1, 1), (1, 0), (2, 1)])
 def test_topk_bit_exact_on_identical_logits(N, K, score, renorm):
     if K > N:
