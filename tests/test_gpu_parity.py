@@ -232,14 +232,21 @@ def test_grouped_swiglu_gathered_rows(dtype, packed):
         assert_close(out[lo:hi], F, dtype, f"F segment {g}")
 
 
+SEG_MANY = [0, 1, 129, 0, 1000, 31, 256, 257, 700, 300, 640, 5, 900, 128, 511, 2]
+# at least 1024 rows per group on average: the two-row-half (256-row tile) shape, with
+# ragged last tiles of 164, 52, 20 and 33 rows and an empty group
+SEG_LARGE = [1700, 0, 2100, 1300, 33]
+
+
+@pytest.mark.parametrize("seg", [SEG_MANY, SEG_LARGE], ids=["many_groups", "large_groups"])
 @pytest.mark.parametrize("gathered", [False, True])
-def test_grouped_swiglu_persistent_shapes(gathered):
+def test_grouped_swiglu_persistent_shapes(gathered, seg):
     """Shapes of the persistent GEMM (d_model, d_ff multiples of 256): ragged groups
     (empty, one row, many 128-row tiles) and more tiles than compute units, so that each
-    workgroup runs several tiles back to back; optionally gathered rows."""
-    say(f"grouped swiglu, persistent-kernel shapes, gathered={gathered}")
-    rng = np.random.default_rng(29 + gathered)
-    seg = [0, 1, 129, 0, 1000, 31, 256, 257, 700, 300, 640, 5, 900, 128, 511, 2]
+    workgroup runs several tiles back to back; few groups of many rows (two row halves
+    per tile); optionally gathered rows."""
+    say(f"grouped swiglu, persistent-kernel shapes, gathered={gathered}, seg={seg}")
+    rng = np.random.default_rng(29 + gathered + 7 * len(seg))
     G, d, dff = len(seg), 768, 1024
     rows = sum(seg)
     offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int32)
