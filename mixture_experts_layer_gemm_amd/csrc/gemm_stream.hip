@@ -11,10 +11,12 @@
 //
 // Schedule (one workgroup of 4 waves per compute unit):
 //   * tiles are ordered (problem, group, n-tile, m-tile); 8 contiguous parts of that list
-//     of equal cost (active 32-row blocks x k stages) go to the 8 XCDs (workgroup b runs
-//     on XCD b % 8) and the workgroups of an XCD take every (grid / 8)-th tile of its
-//     part, so the row tiles that share a weight block run at the same time behind the
-//     same L2;
+//     of equal cost go to the 8 XCDs (workgroup b runs on XCD b % 8) and the workgroups
+//     of an XCD take every (grid / 8)-th tile of its part, so the row tiles that share a
+//     weight block run at the same time behind the same L2. A tile's cost is its bytes
+//     through the compute unit's vector L1 per k stage, in units of one 32-row activation
+//     block: 2 per wave for the weight blocks (fetched whatever the tile's rows) plus one
+//     per active 32-row block, times the k stages;
 //   * every wave streams its NBW weight blocks straight into registers, RS stages
 //     (64 k each) ahead, in a register ring; activations go through a 4-stage LDS ring
 //     filled by direct-to-LDS loads; in the last stages of a tile both rings are already
@@ -134,8 +136,9 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
   const int NG = G0 + (p1.rows > 0 ? 1 : 0);  // groups over both problems (<= 256)
 
   // ---- tile list: per-group tile counts and costs, prefix-summed in LDS ----
-  // cost of a tile = active 32-row blocks x k stages; a group's tiles cost
-  // n-tiles x ceil(rows / 32) x stages in all
+  // cost of a tile = (KW + active 32-row blocks) x k stages; a group's tiles cost
+  // n-tiles x (KW x m-tiles + ceil(rows / 32)) x stages in all
+  constexpr int KW = 2 * C::WAVES;  // weight bytes per stage, in 32-row activation blocks
   for (int g = tid; g <= G0; g += C::THREADS)
     s_off[g] = (p0.offsets != nullptr) ? p0.offsets[g] : (g == 0 ? 0 : p0.rows);
   __syncthreads();
@@ -147,7 +150,7 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
       const StreamProblem& P = tid < G0 ? p0 : p1;
       const int nrows = s_off[tid + 1] - s_off[tid];
       cnt = ceil_div(nrows, C::BM) * (P.Nd / COLS);
-      cost = (P.Nd / COLS) * ceil_div(nrows, 32) * (P.Kd / SK_BKX);
+      cost = (P.Nd / COLS) * (KW * ceil_div(nrows, C::BM) + ceil_div(nrows, 32)) * (P.Kd / SK_BKX);
     }
     s_tstart[tid + 1] = cnt;
     s_cstart[tid + 1] = cost;
@@ -181,12 +184,14 @@ gemm_stream_kernel(StreamProblem p0, StreamProblem p1) {
     }
     const StreamProblem& P = lo < G0 ? p0 : p1;
     const int nrows = s_off[lo + 1] - s_off[lo];
-    const int rb = ceil_div(nrows, 32), mtiles = ceil_div(nrows, C::BM);
+    const int mtiles = ceil_div(nrows, C::BM);
+    const int cn = KW * mtiles + ceil_div(nrows, 32);  // per n-tile, per stage
     const int nst = P.Kd / SK_BKX;
-    const long u = (target - s_cstart[lo] + nst - 1) / nst;  // 32-row blocks into the group
-    int nt = static_cast<int>(u / rb);
-    const int rem = static_cast<int>(u - static_cast<long>(nt) * rb);
-    int mt = ceil_div(rem, C::BM / 32);
+    const long u = (target - s_cstart[lo] + nst - 1) / nst;  // cost per stage into the group
+    int nt = static_cast<int>(u / cn);
+    const int rem = static_cast<int>(u - static_cast<long>(nt) * cn);
+    // every m-tile but the last costs KW + BM / 32: the first m-tile whose prefix reaches rem
+    int mt = ceil_div(rem, KW + C::BM / 32);
     if (mt >= mtiles) {
       ++nt;
       mt = 0;
@@ -566,9 +571,22 @@ bool fits(int mode, const StreamProblem& P) {
 
 }  // namespace
 
+// upper bound of the kernel's summed tile cost (32-bit prefix sums in LDS) for any split
+// of a problem's rows into its G groups: every group adds at most one m-tile and one
+// 32-row block to the unsplit count
+static long cost_bound(int mode, const StreamProblem& P) {
+  if (P.rows <= 0) return 0;
+  using C = SK<kNBW, kXBM, kRS, 1>;
+  const long cols = mode != SK_PLAIN ? C::COLS_SWIGLU : C::COLS_PLAIN;
+  const long kw = 2 * 8, bm = 128;  // the larger weight cost (two row halves), the smaller tile
+  const long mt = (P.rows + bm - 1) / bm + P.G, rb = (P.rows + 31) / 32 + P.G;
+  return (P.Nd / cols) * (kw * mt + rb) * (P.Kd / SK_BKX);
+}
+
 static bool supported(int mode, const StreamProblem& p0, const StreamProblem& p1) {
   if (p0.rows <= 0 || !fits(mode, p0) || !fits(mode, p1)) return false;
   if (p1.rows > 0 && (p1.offsets != nullptr || p1.G != 1 || p0.G + 1 > SK_GT)) return false;
+  if (cost_bound(mode, p0) + cost_bound(mode, p1) >= (1L << 31)) return false;
   return true;
 }
 
