@@ -236,9 +236,13 @@ SEG_MANY = [0, 1, 129, 0, 1000, 31, 256, 257, 700, 300, 640, 5, 900, 128, 511, 2
 # at least 1024 rows per group on average: the two-row-half (256-row tile) shape, with
 # ragged last tiles of 164, 52, 20 and 33 rows and an empty group
 SEG_LARGE = [1700, 0, 2100, 1300, 33]
+# one group holds nearly every row, the rest a row or two: the XCD split falls inside
+# the large group and among tiles of one or two rows
+SEG_SKEW = [1, 0, 2999, 3, 0, 0, 64, 1, 2, 0, 1]
 
 
-@pytest.mark.parametrize("seg", [SEG_MANY, SEG_LARGE], ids=["many_groups", "large_groups"])
+@pytest.mark.parametrize("seg", [SEG_MANY, SEG_LARGE, SEG_SKEW],
+                         ids=["many_groups", "large_groups", "skewed_groups"])
 @pytest.mark.parametrize("gathered", [False, True])
 def test_grouped_swiglu_persistent_shapes(gathered, seg):
     """Shapes of the persistent GEMM (d_model, d_ff multiples of 256): ragged groups
