@@ -370,7 +370,7 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
   MOE_ROUTE_CASE(16, 2, 8, 8)
   MOE_ROUTE_CASE(16, 4, 8, 4)
   MOE_ROUTE_CASE(16, 8, 8, 2)
-  MOE_ROUTE_CASE(32, 17, 4, 1)
+  MOE_ROUTE_CASE(32, 17, 4, 2)
 #undef MOE_ROUTE_CASE
   return hipErrorInvalidValue;
 }
