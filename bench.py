@@ -343,6 +343,10 @@ def main():
                    "kept_routes": R, "active_experts": act_experts},
         "expert_gemm_tflops": round(expert_tflops, 1),
         "expert_gemm_frac_bf16_peak": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
+        # the routed experts (kept routes only) and the shared MLP run in the same two
+        # launches, so the rate above is over both; their flops apart:
+        "expert_gemm_gflop": {"routed_kept": round(6.0 * R * d * d_r / 1e9, 1),
+                              "shared": round(6.0 * T * d * d_s / 1e9, 1)},
         "roofline": dict(kernel="gate/up pass: routed experts (gathered rows) + shared MLP, "
                          "SwiGLU fused (gemm_stream_kernel<2,4,4,1,1>)" if pk else
                          "routed gate/up grouped GEMM (row-major weights)",
