@@ -185,9 +185,19 @@ def test_selected_outrank_unselected():
 
 
 def test_shared_gate_is_sigmoid_of_projection():
-    x = np.array([[1.0, -2.0], [0.0, 0.0]])
+    """p2 Table 52, Qwen rows: the learned shared gate is a sigmoid of one projection of
+    x. Closed forms: sigma(0) = 1/2, sigma(2) = 1/(1 + e^-2), sigma(-1) = 1/(1 + e), and
+    sigma(u) + sigma(-u) = 1, so a flipped sign or 1 - sigma fails the nonzero rows."""
+    x = np.array([[1.0, -2.0], [0.0, 0.0], [4.0, 0.0], [1.0, 2.0], [-3.0, -4.0]])
     w = np.array([0.5, 0.25])
-    assert np.allclose(O.shared_gate(x, w), [0.5, 0.5])
+    # projections: 0, 0, 2, 1, -2.5
+    s = O.shared_gate(x, w)
+    assert s[0] == 0.5 and s[1] == 0.5
+    assert abs(s[2] - 0.8807970779778823) < 1e-15          # 1 / (1 + exp(-2))
+    assert abs(s[3] - 0.7310585786300049) < 1e-15          # 1 / (1 + exp(-1))
+    assert abs(s[4] - 1.0 / (1.0 + math.exp(2.5))) < 1e-15
+    w2 = np.array([-1.0, 0.0])
+    assert abs(O.shared_gate(np.array([[1.0, 7.0]]), w2)[0] - 0.2689414213699951) < 1e-15
 
 
 def test_silu_values():
@@ -380,7 +390,7 @@ def test_forward_tokens_matches_whole_layer():
 
 def test_forward_scale_matches_eq85():
     """p1 Section 21.3: at random init the MoE/dense mean-square output ratio follows
-    Eq. 85 (statistical check, +-6%), and the Table 37 conventions reproduce the four
+    Eq. 85 (statistical check, +-3%), and the Table 37 conventions reproduce the four
     Figure 70(a) RMS ratios from E[sum p^2] = 0.2589."""
     g = golden("fig70_forward_scale.json")
     d_r, d_s, K = g["d_r"], g["d_s"], g["K"]
@@ -412,11 +422,36 @@ def test_forward_scale_matches_eq85():
             dense_swiglu(x[t:t + 1], *sh[0])[0]
         pred += eq85_ratio(dr, ds, res.r[t].tolist(), 1.0)
     measured = np.sum(res.y ** 2) / np.sum(dense ** 2)
-    assert measured == pytest.approx(pred / T, rel=0.06)
+    assert measured == pytest.approx(pred / T, rel=0.03)
     # branch scale follows intermediate width: RMS(g) / RMS(f_i) ~ sqrt(d_s / d_r)
     shared_rms = np.sqrt(np.mean(res.G ** 2))
     routed_rms = np.sqrt(np.mean(res.F_perm ** 2))
-    assert shared_rms / routed_rms == pytest.approx(math.sqrt(ds / dr), rel=0.05)
+    assert shared_rms / routed_rms == pytest.approx(math.sqrt(ds / dr), rel=0.03)
+
+
+def test_weight_removed_differs_from_route_drop_fraction():
+    """p5 Section 10.3 asks for the selected mixture weight removed by dropping beside the
+    route-drop fraction of Eq. 27; for K > 1 they differ. Hand case, N = 3, K = 2,
+    capacity 1, first-come by token: token 0 routes to experts (2, 0) with r = (0.5, 0.5),
+    token 1 to (1, 0) with r = (0.9, 0.1). Expert 0 is full after token 0, so only the
+    r = 0.1 route drops: delta = 1/4, weight removed = 0.1 / 2.0 = 0.05, one token loses
+    a route and none loses both. Second case (r = (3, 1) per token, the r = 3 route of
+    token 1 dropped): weight removed = 3/8 against delta = 1/4."""
+    idx = np.array([[2, 0], [1, 0]], dtype=np.int32)
+    r = np.array([[0.5, 0.5], [0.9, 0.1]])
+    kept = O.keep_routes(idx, 3, 1)
+    assert kept.tolist() == [[True, True], [True, False]]
+    p = np.full((2, 3), 1.0 / 3.0)
+    st = O.balance_stats(p, idx, kept, r, 3)
+    assert st.delta_route == 0.25
+    assert abs(st.weight_removed - 0.05) < 1e-15
+    assert st.tokens_lost_any == 1 and st.tokens_lost_all == 0
+    idx2 = np.array([[1, 0], [1, 2]], dtype=np.int32)
+    r2 = np.array([[3.0, 1.0], [3.0, 1.0]])
+    kept2 = O.keep_routes(idx2, 3, 1)
+    assert kept2.tolist() == [[True, True], [False, True]]
+    st2 = O.balance_stats(p, idx2, kept2, r2, 3)
+    assert st2.delta_route == 0.25 and abs(st2.weight_removed - 0.375) < 1e-15
 
 
 # --------------------------------------------------------------------------------------
@@ -448,9 +483,20 @@ def _coeff_without_alpha(z, idx, score, renorm, alpha):
     return _orig_coeff(z, idx, score, renorm, 1.0)
 
 
+def _shared_gate_flipped(x, w):
+    return 1.0 / (1.0 + np.exp(np.asarray(x, np.float64) @ np.asarray(w, np.float64)))
+
+
+def _stats_weight_removed_is_delta(p, idx, kept, r, N, group=0):
+    st = _orig_stats(p, idx, kept, r, N, group)
+    st.weight_removed = st.delta_route
+    return st
+
+
 _orig_combine = O.combine
 _orig_keep = O.keep_routes
 _orig_coeff = O.route_coefficients
+_orig_stats = O.balance_stats
 
 MUTATIONS = {
     "gate/up swapped": ("swiglu", _swiglu_transposed_gate,
@@ -466,6 +512,11 @@ MUTATIONS = {
                         test_keep_closed_form_and_permutation_invariants]),
     "alpha ignored": ("route_coefficients", _coeff_without_alpha,
                       [test_fig69_olmo_rule_worked_example, test_coefficient_sums_per_mode]),
+    "shared gate sign flipped": ("shared_gate", _shared_gate_flipped,
+                                 [test_shared_gate_is_sigmoid_of_projection]),
+    "weight removed is the route-drop fraction": (
+        "balance_stats", _stats_weight_removed_is_delta,
+        [test_weight_removed_differs_from_route_drop_fraction]),
 }
 
 
