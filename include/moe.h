@@ -171,6 +171,32 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_gro
                 int max_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_permute_noalloc: moe_permute with its scratch (chunk histograms and in-chunk
+ * ranks) in a fixed device array of the library instead of a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Arguments, outputs and errors are
+ * those of moe_permute without `workspace` / `workspace_bytes`; nothing is allocated or
+ * freed.
+ *
+ *   limit              moe_permute_workspace_size(T, N, K) = 4 N ceil(T / 64) + 4 T K
+ *                      bytes (each part rounded up to 256) must not exceed
+ *                      MOE_NOALLOC_SCRATCH_BYTES, else MOE_ERR_WORKSPACE (nothing is
+ *                      enqueued); e.g. T = 65536 tokens at N = 256, K = 16 need 5 MiB.
+ *   sharing            every GPU holds one such array from the library's first call on
+ *                      it until the process ends; all calls on a GPU use it, so calls
+ *                      that overlap on one GPU (other streams, other host threads)
+ *                      race. Nothing in it needs clearing: each call writes the
+ *                      histograms and ranks it reads.
+ *   device             the array is resolved for the current device on the first call
+ *                      there (hipGetSymbolAddress); a failure returns MOE_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_permute_noalloc(int T, int d_model, int N, int K, int capacity, int capacity_group,
+                        int dt, const void* x, const int32_t* topk_idx, int32_t* C_req,
+                        int32_t* C_keep, int32_t* offsets, int32_t* dest_row,
+                        int32_t* row_token, void* x_perm, int max_rows, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_grouped_swiglu: G SwiGLU experts over densely packed row segments, as a grouped
  * GEMM over the real counts (no padding rows):
  *   for each group g, rows r in [offsets[g], offsets[g+1]):

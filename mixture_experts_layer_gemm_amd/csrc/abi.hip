@@ -4,6 +4,7 @@
 #include <climits>
 #include <cmath>
 #include <cstddef>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -213,6 +214,56 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_gro
   if (!workspace || workspace_bytes < moe_permute_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
   CountWs w{};
   carve_count(workspace, T, N, K, false, &w);
+  MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
+  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
+                      stream));
+  MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
+                         dest_row, row_token, x_perm, stream));
+  return MOE_OK;
+}
+
+// ---- allocation-free permute: scratch in a fixed device array ----------------------
+// Each device the library runs on holds its own copy of `scratch` (one code object per
+// device). Host code never passes the array's name to a kernel (on the host that name is
+// a stand-in, not a device address): the device address of each copy is looked up once,
+// with that device current, and kept per device.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// device address of the current device's scratch array, or nullptr
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+int moe_permute_noalloc(int T, int d_model, int N, int K, int capacity, int capacity_group,
+                        int dt, const void* x, const int32_t* topk_idx, int32_t* C_req,
+                        int32_t* C_keep, int32_t* offsets, int32_t* dest_row,
+                        int32_t* row_token, void* x_perm, int max_rows, hipStream_t stream) {
+  MOE_TRY(check_router_dims(T, d_model, N, K));
+  MOE_TRY(check_dtype(dt));
+  MOE_TRY(check_group(N, capacity_group));
+  if (!x || !topk_idx || !C_req || !C_keep || !offsets || !dest_row || !row_token)
+    return MOE_ERR_INVALID_ARG;
+  if (max_rows < moe_max_rows(T, N, K, capacity, capacity_group)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (moe_permute_workspace_size(T, N, K) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  CountWs w{};
+  carve_count(ws, T, N, K, false, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
                       stream));

@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "moe_backward": (I, [P, P, S, P]),
         "moe_permute_workspace_size": (S, [I, I, I]),
         "moe_permute": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, S, P]),
+        "moe_permute_noalloc": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, P]),
         "moe_grouped_swiglu": (I, [I, I, I, I, I, P, I, P, P, I, P, P, P, P, P, P]),
         "moe_grouped_gemm": (I, [I, I, I, I, I, I, P, I, P, P, I, P, P, P, P]),
         "moe_pack_weights": (I, [I, I, I, I, P, P, P]),
@@ -216,6 +217,32 @@ def moe_permute(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True,
                          _ptr(out["dest_row"]), _ptr(out["row_token"]), _ptr(out["x_perm"]),
                          max(rows, 1), _ptr(ws), ws.numel(), _stream())
     _check("moe_permute", st)
+    return out
+
+
+def moe_permute_noalloc(x, topk_idx, N: int, capacity: int = -1, copy_rows: bool = True,
+                        capacity_group: int = 0, out=None):
+    """moe_permute with its scratch in the library's fixed device array (no workspace).
+    `out` (a dict as moe_permute returns) supplies the output buffers; the library
+    itself allocates nothing."""
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    rows = max_rows(T, N, K, capacity, capacity_group)
+    if out is None:
+        out = dict(C_req=torch.empty(N, dtype=torch.int32, device=dev),
+                   C_keep=torch.empty(N, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
+                   dest_row=torch.empty(T, K, dtype=torch.int32, device=dev),
+                   row_token=torch.empty(max(rows, 1), dtype=torch.int32, device=dev),
+                   x_perm=(torch.empty(max(rows, 1), d, dtype=x.dtype, device=dev)
+                           if copy_rows else None))
+    st = lib.moe_permute_noalloc(T, d, N, K, capacity, capacity_group, _dt(x), _ptr(x),
+                                 _ptr(topk_idx), _ptr(out["C_req"]), _ptr(out["C_keep"]),
+                                 _ptr(out["offsets"]), _ptr(out["dest_row"]),
+                                 _ptr(out["row_token"]), _ptr(out.get("x_perm")),
+                                 out["row_token"].numel(), _stream())
+    _check("moe_permute_noalloc", st)
     return out
 
 

@@ -14,7 +14,7 @@ EXPECTED = ["moe_backward", "moe_backward_workspace_size",
             "moe_capacity_from_factor", "moe_combine", "moe_experts", "moe_forward",
             "moe_forward_workspace_size",
             "moe_grouped_gemm", "moe_grouped_swiglu", "moe_max_rows", "moe_pack_weights",
-            "moe_pack_weights_transposed", "moe_permute",
+            "moe_pack_weights_transposed", "moe_permute", "moe_permute_noalloc",
             "moe_permute_workspace_size", "moe_rank_capacity_from_factor",
             "moe_route", "moe_route_workspace_size", "moe_status_string"]
 
@@ -212,3 +212,29 @@ def test_backward_rejects_bad_arguments_without_launching():
     assert P(2, 96, 128, 128, 1, 1, None, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
     assert P(2, 64, 128, 128, 0, 1, None, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED  # fp32
     assert P(2, 64, 128, 128, 1, 4096, None, 4096 + 64, None) == moe.MOE_ERR_INVALID_ARG  # overlap
+
+
+def test_noalloc_permute_rejects_oversize_and_bad_arguments_without_launching():
+    """The allocation-free permute checks its arguments and the fixed scratch size before
+    it touches the device: a shape whose histograms and ranks exceed the 8 MiB array is
+    refused with MOE_ERR_WORKSPACE; T = 0 is a no-op."""
+    lib = moe.lib
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below returns first
+    T, N, K = 1 << 20, 256, 16
+    need = lib.moe_permute_workspace_size(T, N, K)
+    assert need > (8 << 20)
+    big = lib.moe_max_rows(T, N, K, -1, 0)
+    st = lib.moe_permute_noalloc(T, 2048, N, K, -1, 0, moe.MOE_BF16, fake, fake, fake, fake,
+                                 fake, fake, fake, None, big, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    # bad arguments: K > N, NULL outputs, max_rows too small, a group not dividing N
+    assert lib.moe_permute_noalloc(64, 256, 4, 5, -1, 0, moe.MOE_BF16, fake, fake, fake, fake,
+                                   fake, fake, fake, None, 1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_noalloc(64, 256, 8, 2, -1, 0, moe.MOE_BF16, fake, fake, None, fake,
+                                   fake, fake, fake, None, 1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_noalloc(64, 256, 8, 2, -1, 0, moe.MOE_BF16, fake, fake, fake, fake,
+                                   fake, fake, fake, None, 127, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_noalloc(64, 256, 8, 2, 10, 3, moe.MOE_BF16, fake, fake, fake, fake,
+                                   fake, fake, fake, None, 1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_noalloc(0, 256, 8, 2, -1, 0, moe.MOE_BF16, fake, fake, fake, fake,
+                                   fake, fake, fake, None, 0, None) == moe.MOE_OK
