@@ -1,12 +1,9 @@
 """GPU parity at the full sizes of the five workloads, in the launch configuration that
-bench.py times (one moe_forward on device-resident inputs).
-
-The Olmo-style and capacity-limited layers (T=4096, d_model=2048, 64 experts) are
-checked against the whole-layer oracle. The 256-expert and 8 x 14336 layers are too
-slow for the fp64 oracle in full: there every integer stage is still compared in full
-(top-K from the GPU's fp32 logits, counts, offsets, restoration map, row owners, packed
-rows), and the float stages on sampled tokens and sampled rows of sampled experts,
-which the oracle computes one by one.
+bench.py times (one moe_forward on device-resident inputs), against the whole-layer
+oracle: routing bit-exact (top-K from the GPU's fp32 logits, counts, offsets,
+restoration map, row owners), every expert's H and F segment, the shared output G and
+y over every token within the bf16 bound. The fp64 oracle takes about 20 s (256 experts)
+and 40 s (8 x 14336) of host BLAS at these sizes and a few GB of host memory.
 """
 import numpy as np
 import pytest
@@ -31,8 +28,8 @@ def _layer(name):
     return L
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["C1", "C4A", "C4B"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4A", "C4B"])
 def test_full_layer_whole_oracle(name):
     from tests.test_gpu_parity import check_forward, setup_module as sm
     sm(None)
@@ -50,37 +47,3 @@ def test_full_layer_whole_oracle(name):
         say(f"  capacity {L.capacity}: kept {int(C_keep.sum())}, dropped {dropped} of {int(C_req.sum())}, "
             f"active experts {int((C_keep > 0).sum())}")
         assert dropped > 0
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["C2", "C3"])
-def test_full_layer_sampled(name):
-    from tests.test_gpu_parity import check_forward, setup_module as sm
-    sm(None)
-    L = _layer(name)
-    rng = np.random.default_rng(7)
-    toks = sorted(rng.choice(L.T, size=12, replace=False).tolist()) + [0, L.T - 1]
-    lay = check_forward(L, full=False, sample_tokens=toks)
-    # sampled rows of sampled experts for the two GEMM passes
-    o = lay.out
-    offs = host(o["offsets"])
-    Hg = o["h_perm"]
-    Fg = o["f_perm"]
-    row_token = o["row_token"]
-    c = L.cfg
-    experts = sorted(set(rng.choice(c.N, size=min(4, c.N), replace=False).tolist()))
-    for e in experts:
-        lo, hi = int(offs[e]), int(offs[e + 1])
-        if hi <= lo:
-            continue
-        rows = sorted(set(rng.integers(lo, hi, size=min(16, hi - lo)).tolist()))
-        ri = torch.tensor(rows, device="cuda")
-        X = host(L.x[row_token[ri].long()])
-        H, F = O.swiglu(X, *L.inp.expert_f32(e))
-        assert_close(host(Hg[ri]), H, "bf16", f"H rows of expert {e}")
-        assert_close(host(Fg[ri]), F, "bf16", f"F rows of expert {e}")
-        say(f"  expert {e}: {len(rows)} sampled rows ok")
-    if c.d_s:
-        tt = torch.tensor(toks, device="cuda")
-        G = O.shared_output(L.x_f()[toks], L.inp.shared_f32())
-        assert_close(host(o["g"][tt]), G, "bf16", "shared output (sampled tokens)")
