@@ -9,6 +9,13 @@ one JSON line: whole-layer tokens/s, the expert-GEMM TFLOP/s, the roofline of th
 dominant kernel (the gate/up pass: routed experts with gathered rows plus the shared
 MLP, one persistent launch, SwiGLU fused), per-stage times and the CPU oracle timed on a
 bounded sample of the same workload.
+
+Timing: W warm-up steps, then the K timed steps as K forward calls captured in one HIP
+graph and replayed once between synchronizations (value, ms_per_step); beside it the
+same forward with one graph replay per step (mean over K, and the median of at least 50
+individually timed replays), and eager launches. Stage times are medians of 50 graph
+replays. --profile-forward N only replays the one-step graph N times, for a kernel trace
+of forward steps alone.
 """
 from __future__ import annotations
 
@@ -59,9 +66,8 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def time_graph(torch, fn, reps: int) -> float:
-    """Average GPU time (ms) of fn() over `reps` calls captured in one HIP graph and
-    replayed, bracketed by events on the replay stream."""
+def capture(torch, fn, calls: int = 1):
+    """fn() called `calls` times, captured once in a HIP graph (warmed on a side stream)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -70,28 +76,80 @@ def time_graph(torch, fn, reps: int) -> float:
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(reps):
+        for _ in range(calls):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return g
 
 
-def time_eager(torch, fn, reps: int) -> float:
-    fn()
+def replay_times(torch, g, reps: int) -> list:
+    """GPU time (ms) of each of `reps` back-to-back replays of graph g, every replay
+    bracketed by its own pair of events on the replay stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def time_median(torch, fn, reps: int, calls: int = 1) -> float:
+    """Median GPU time (ms) of one fn() call: `reps` timed replays of a graph holding
+    `calls` calls (several calls per replay for kernels of a few microseconds, so that a
+    replay's launch does not enter its own timing)."""
+    g = capture(torch, fn, calls)
+    return float(np.median(replay_times(torch, g, reps))) / calls
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gfx_clock_during(torch, g, seconds: float):
+    """Median shader (GFX) clock in MHz sampled through amdsmi while graph g replays
+    back to back for about `seconds`; None where amdsmi is not available."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+    except Exception:  # pragma: no cover - no SMI library or device
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append(float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]))
+            except Exception:
+                pass
+            time.sleep(0.005)
+
+    one = float(np.median(replay_times(torch, g, 5)))
+    n = max(20, int(seconds * 1e3 / max(one, 1e-3)))
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    for _ in range(n):
+        g.replay()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    keep = samples[len(samples) // 5:]  # drop the ramp at the start of the window
+    return float(np.median(keep)) if keep else None
 
 
 def time_cold(torch, fn, reps: int, scratch) -> float:
@@ -134,6 +192,7 @@ def cpu_baseline(inp, sample_tokens: int):
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{sample_tokens} of {c.T} tokens of the same layer (all {c.N} experts), fp64 "
                       f"NumPy forward only, median of {len(times)} runs of {dt:.1f} s"}
 
@@ -144,7 +203,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C1")
-    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--stage-reps", type=int, default=50,
+                    help="timed replays per stage (the median is reported)")
+    ap.add_argument("--profile-forward", type=int, default=0, metavar="N",
+                    help="only replay the captured forward N times after the warmup (for a "
+                         "kernel trace of forward steps alone) and print one timing line")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -196,24 +259,53 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    # eager: every step enqueues the forward's kernels one by one
-    ms_eager = timed(layer.forward)
-    ms = ms_eager
-    if not args.eager:
-        # the same forward captured once in a HIP graph; each step is one replay
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            layer.forward()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            layer.forward()
+    # the forward captured once in a HIP graph; each step is one replay
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward()
+    if args.profile_forward > 0:
         for _ in range(args.warmup):
             graph.replay()
-        ms = timed(graph.replay)
+        torch.cuda.synchronize()
+        t = replay_times(torch, graph, args.profile_forward)
+        print(json.dumps({"mode": "forward graph replays only", "workload": cfg.name,
+                          "replays": len(t), "ms_median": round(float(np.median(t)), 4),
+                          "ms_mean": round(float(np.mean(t)), 4)}), flush=True)
+        return
+
+    # eager: every step enqueues the forward's kernels one by one
+    ms_eager = timed(layer.forward)
+    for _ in range(args.warmup):
+        graph.replay()
+    # one forward per graph replay: each step pays the replay's launch
+    ms_each = timed(graph.replay)
+    ms = ms_eager
+    if not args.eager:
+        # the timed K steps: K forward calls captured back to back in one graph and
+        # replayed once, as the layers of a model step run back to back
+        graph_k = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_k):
+            for _ in range(args.steps):
+                layer.forward()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        graph_k.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        del graph_k
     tokens_per_s = T / (ms / 1e3)
+    # per-step spread: one forward per replay, every replay timed on its own, at least 50
+    step_times = replay_times(torch, graph, max(50, args.steps))
+    ms_median = float(np.median(step_times))
 
     # ---- per-stage timing on the layer's own buffers ------------------------------
     o = layer.out
@@ -231,24 +323,34 @@ def main():
                 h_shared=torch.empty(T, d_s, dtype=x.dtype, device=x.device) if d_s else None,
                 g=torch.empty(T, d, dtype=x.dtype, device=x.device) if d_s else None)
 
-    def experts(pass_):
+    def experts(pass_, with_shared=True):
         return lambda: moe.moe_experts(x, o["row_token"], o["offsets"], rows, lw["w_gate"],
-                                       lw["w_up"], lw["w_down"], shared=sm, out=bufs,
-                                       packed=pk, pass_=pass_)
-    # the dominant kernel: the gate/up pass, timed with events on its own stream
-    st["experts_gateup_ms"] = time_eager(torch, experts(1), reps)
-    st["experts_down_ms"] = time_eager(torch, experts(2), reps)
-    logits = torch.empty(T, N, dtype=torch.float32, device=x.device)
-    st["route_ms"] = time_graph(torch, lambda: moe.moe_route(
+                                       lw["w_up"], lw["w_down"], shared=sm if with_shared else None,
+                                       out=bufs, packed=pk, pass_=pass_)
+    # the dominant kernel: the gate/up pass (routed experts + shared MLP, one launch), each
+    # replay timed with events on the stream it runs on; medians over `reps` replays
+    st["experts_gateup_ms"] = time_median(torch, experts(1), reps)
+    st["experts_down_ms"] = time_median(torch, experts(2), reps)
+    # the same passes with the routed experts alone and the shared MLP alone
+    apart = {"routed_gateup_ms": time_median(torch, experts(1, False), reps),
+             "routed_down_ms": time_median(torch, experts(2, False), reps)}
+    if sm is not None:
+        apart["shared_gateup_ms"] = time_median(torch, lambda: moe.moe_grouped_gemm(
+            x, None, sm[0][None], sm[1][None], out=bufs["h_shared"], swiglu=True, packed=pk), reps)
+        apart["shared_down_ms"] = time_median(torch, lambda: moe.moe_grouped_gemm(
+            bufs["h_shared"], None, sm[2][None], out=bufs["g"], swiglu=False, packed=pk), reps)
+    # shader clock while the gate/up pass replays back to back for about a second
+    clock_mhz = gfx_clock_during(torch, capture(torch, experts(1)), 1.0)
+    st["route_ms"] = time_median(torch, lambda: moe.moe_route(
         x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
-        w_shared_gate=gate, want_counts=False), reps)
+        w_shared_gate=gate, want_counts=False), reps, calls=10)
     idx = o["topk_idx"]
-    st["permute_ms"] = time_graph(torch, lambda: moe.moe_permute(x, idx, N, cap, copy_rows=False),
-                                  reps)
+    st["permute_ms"] = time_median(torch, lambda: moe.moe_permute(x, idx, N, cap, copy_rows=False),
+                                   reps, calls=10)
     y2 = torch.empty_like(layer.y)
-    st["combine_ms"] = time_graph(torch, lambda: moe.moe_combine(
+    st["combine_ms"] = time_median(torch, lambda: moe.moe_combine(
         o["f_perm"], o["dest_row"], o["topk_r"], o.get("g"), s=cfg.s, s_tok=o.get("s_tok"), y=y2),
-        reps)
+        reps, calls=10)
 
     # the same three stages with cold caches (a 512 MB read before each call)
     scratch = torch.ones(128 << 20, dtype=torch.float32, device=x.device)
@@ -267,19 +369,19 @@ def main():
     # of N/8 experts, capacity factor 1), biased selection and the bias controller
     nx = {}
     z_l = o["logits"]
-    nx["balance_stats_ms"] = time_graph(torch, lambda: moe.moe_balance_stats(
-        z_l, o["C_req"], o["C_keep"], o["dest_row"], o["topk_r"], score=cfg.score), reps)
+    nx["balance_stats_ms"] = time_median(torch, lambda: moe.moe_balance_stats(
+        z_l, o["C_req"], o["C_keep"], o["dest_row"], o["topk_r"], score=cfg.score), reps, calls=10)
     grp = N // 8 if N % 8 == 0 else N
     rcap = moe.rank_capacity_from_factor(1.0, K, -(-T // (N // grp)))
-    nx["permute_rank_capacity_ms"] = time_graph(torch, lambda: moe.moe_permute(
-        x, idx, N, rcap, copy_rows=False, capacity_group=grp), reps)
+    nx["permute_rank_capacity_ms"] = time_median(torch, lambda: moe.moe_permute(
+        x, idx, N, rcap, copy_rows=False, capacity_group=grp), reps, calls=10)
     eb = torch.linspace(-0.5, 0.5, N, device=x.device, dtype=torch.float32)
-    nx["route_biased_ms"] = time_graph(torch, lambda: moe.moe_route(
+    nx["route_biased_ms"] = time_median(torch, lambda: moe.moe_route(
         x, w_router, K, score=cfg.score, renorm=cfg.renorm, alpha=cfg.alpha, logit_bias=bias,
-        w_shared_gate=gate, want_counts=False, expert_bias=eb), reps)
+        w_shared_gate=gate, want_counts=False, expert_bias=eb), reps, calls=10)
     acc = o["C_req"].clone()
-    nx["bias_update_ms"] = time_eager(torch, lambda: moe.moe_bias_update(acc, eb, 1e-3, reset=False),
-                                      reps)
+    nx["bias_update_ms"] = time_median(torch, lambda: moe.moe_bias_update(acc, eb, 1e-3, reset=False),
+                                       reps, calls=10)
     nx_bytes = {"balance_stats": T * N * 4 + T * K * 8 + 8 * N}
     # f4: fixed-router backward on the same batch (recompute A, B; dH; dX; weight gradients)
     bwd_flops = None
@@ -289,7 +391,7 @@ def main():
                                logit_bias=bias, w_shared_gate=gate, shared=shared, trainable=True)
         layer_t.forward()
         dy = torch.randn(T, d, device=x.device, dtype=torch.float32).to(torch.bfloat16)
-        nx["backward_ms"] = time_eager(torch, lambda: layer_t.backward(dy), max(3, reps // 4))
+        nx["backward_ms"] = time_median(torch, lambda: layer_t.backward(dy), max(5, reps // 5))
         R_t = int(layer_t.out["offsets"][-1].item())
         bwd_flops = 16.0 * R_t * d * d_r + 16.0 * T * d * (layer_t.shared_mlp[0].shape[0]
                                                            if layer_t.shared_mlp else 0)
@@ -321,6 +423,21 @@ def main():
     }
     hbm = {k: b / (st[k + "_ms"] * 1e-3) / 1e9 for k, b in stage_bytes.items()}
     hbm_cold = {k: b / (cold[k + "_ms"] * 1e-3) / 1e9 for k, b in stage_bytes.items()}
+    # the persistent GEMM takes two row halves (8 waves, 2 weight stages in flight) when
+    # the packed bound holds at least 1024 rows per group, else one (4 waves, 4 stages)
+    rh2 = rows >= 1024 * N
+    kernel_label = ("gate/up pass: routed experts (gathered rows) + shared MLP, SwiGLU fused "
+                    "(gemm_stream_kernel<2,4,%s,1>)" % ("2,2" if rh2 else "4,1")) if pk else \
+        "routed gate/up grouped GEMM (row-major weights)"
+    routed_flops = 6.0 * R * d * d_r
+    t_routed = (apart["routed_gateup_ms"] + apart["routed_down_ms"]) * 1e-3
+    gemm = {"routed_kept_tflops": round(routed_flops / t_routed / 1e12, 1),
+            "routed_kept_frac_bf16_peak": round(routed_flops / t_routed / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "passes_ms": {k.replace("_ms", ""): round(v, 4) for k, v in apart.items()}}
+    if d_s:
+        shared_flops = 6.0 * T * d * d_s
+        t_sh = (apart["shared_gateup_ms"] + apart["shared_down_ms"]) * 1e-3
+        gemm["shared_tflops"] = round(shared_flops / t_sh / 1e12, 1)
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -330,7 +447,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager": round(ms_eager, 4),
-        "launch": "eager" if args.eager else "hip_graph",
+        "ms_per_step_one_per_replay": round(ms_each, 4),
+        "ms_per_step_one_per_replay_median": round(ms_median, 4),
+        "step_reps": len(step_times),
+        "launch": "eager" if args.eager else "hip_graph: the K timed steps captured in one graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -347,9 +467,15 @@ def main():
         # launches, so the rate above is over both; their flops apart:
         "expert_gemm_gflop": {"routed_kept": round(6.0 * R * d * d_r / 1e9, 1),
                               "shared": round(6.0 * T * d * d_s / 1e9, 1)},
-        "roofline": dict(kernel="gate/up pass: routed experts (gathered rows) + shared MLP, "
-                         "SwiGLU fused (gemm_stream_kernel<2,4,4,1,1>)" if pk else
-                         "routed gate/up grouped GEMM (row-major weights)",
+        # the same work in launches of its own: the routed experts alone (6 d d_r per kept
+        # route over their two passes) and the shared MLP alone
+        "grouped_gemm_apart": gemm,
+        "shader_clock_mhz": None if clock_mhz is None else round(clock_mhz),
+        "peak_bf16_at_clock_tflops": (None if clock_mhz is None else
+                                      round(PEAK_BF16_TFLOPS * clock_mhz / 2400.0, 1)),
+        "stage_timing": f"median of {reps} graph replays per stage (route, permute, combine and "
+                        "the short next rows: 10 calls per replay)",
+        "roofline": dict(kernel=kernel_label, time="median of %d replays" % reps,
                          **roof, algorithmic_bytes=bytes_gateup, flops_per_launch=flops_gateup,
                          mfma_tflops=round(flops_gateup / t_gateup / 1e12, 1),
                          mfma_frac=round(flops_gateup / t_gateup / 1e12 / PEAK_BF16_TFLOPS, 4)),
@@ -366,7 +492,17 @@ def main():
     # what a plain streaming read reaches on this GPU (row sums over 1 GiB of fp32 that no
     # cache holds), the practical ceiling beside the 8 TB/s spec figure
     probe = torch.ones(256 << 20, dtype=torch.float32, device=x.device).view(-1, 4096)
-    probe_ms = time_eager(torch, lambda: probe.sum(dim=1), 5)
+    probe.sum(dim=1)
+    torch.cuda.synchronize()
+    pt = []
+    for _ in range(5):   # eager: a torch reduction is not captured in a graph here
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        probe.sum(dim=1)
+        e1.record()
+        torch.cuda.synchronize()
+        pt.append(e0.elapsed_time(e1))
+    probe_ms = float(np.median(pt))
     out["hbm_read_probe_gbs"] = round(probe.numel() * 4 / (probe_ms * 1e-3) / 1e9, 1)
     del probe
     torch.cuda.synchronize()
