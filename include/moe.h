@@ -114,9 +114,13 @@ int moe_max_rows(int T, int N, int K, int capacity, int capacity_group);
  *   topk_r             [T][K] float32 out: routed coefficients r
  *   s_tok              [T] float32 out, or NULL (required iff w_shared_gate != NULL)
  *   C_req              [N] int32 out, or NULL
- *   workspace          moe_route_workspace_size(T, N, K) bytes (may be NULL if 0)
+ *   workspace          moe_route_workspace_size(T, d_model, N, K) bytes; needed when C_req
+ *                      is given, and for bf16 logits of more than 128 experts without a
+ *                      shared gate (N a multiple of 64, d_model a multiple of 256): those
+ *                      are computed split over d_model slices (partial logits, summed in
+ *                      a fixed order) from a copy of w_router packed in the workspace
  * ------------------------------------------------------------------------------- */
-size_t moe_route_workspace_size(int T, int N, int K);
+size_t moe_route_workspace_size(int T, int d_model, int N, int K);
 int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
               const void* x, const void* w_router, const float* logit_bias,
               const float* expert_bias, const void* w_shared_gate, float* logits,

@@ -57,21 +57,27 @@ size_t esize(int dt) { return dt == MOE_BF16 ? 2 : 4; }
   } while (0)
 
 // Workspace layout shared by moe_route and moe_permute: chunk histograms and
-// in-chunk ranks, then (route only) scratch for C_keep/offsets.
+// in-chunk ranks, then (route only) scratch for C_keep/offsets and the split-K logit
+// slices of routers with many experts.
 struct CountWs {
   int32_t* hist;
   int32_t* loc_rank;
   int32_t* c_keep;
   int32_t* offsets;
+  void* route_scratch;  // split-K logits of many experts (moe_route only)
 };
 
-size_t carve_count(void* ws, int T, int N, int K, bool with_scan_scratch, CountWs* out) {
+// d_model < 0: no route scratch (moe_permute)
+size_t carve_count(void* ws, int T, int d_model, int N, int K, CountWs* out) {
   Carver c(ws);
   CountWs w;
+  const bool route = d_model >= 0;
   w.hist = c.take<int32_t>(static_cast<size_t>(nchunks_of(T)) * N);
   w.loc_rank = c.take<int32_t>(static_cast<size_t>(T) * K);
-  w.c_keep = with_scan_scratch ? c.take<int32_t>(N) : nullptr;
-  w.offsets = with_scan_scratch ? c.take<int32_t>(N + 1) : nullptr;
+  w.c_keep = route ? c.take<int32_t>(N) : nullptr;
+  w.offsets = route ? c.take<int32_t>(N + 1) : nullptr;
+  const size_t rb = route ? route_scratch_bytes(T, d_model, N) : 0;
+  w.route_scratch = rb ? static_cast<void*>(c.take<char>(rb)) : nullptr;
   if (out) *out = w;
   return c.off;
 }
@@ -84,6 +90,7 @@ struct FwdWs {
   void *x_perm, *h_perm, *f_perm, *g, *h_shared;
   float* logits;     // needed by the balance statistics
   void* stats_ws;
+  void* route_scratch;  // split-K logits of routers with many experts
 };
 
 size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
@@ -117,6 +124,9 @@ size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
   const bool stats = a->balance_P != nullptr && a->balance_stats != nullptr;
   w.logits = a->logits ? a->logits : (stats ? c.take<float>(T * N) : nullptr);
   w.stats_ws = stats ? static_cast<void*>(c.take<char>(stats_workspace_bytes(a->T, a->N))) : nullptr;
+  const size_t rb = route_split_slices(a->N, a->d_model, a->dt, 0, a->w_shared_gate != nullptr) > 0
+                        ? route_scratch_bytes(a->T, a->d_model, a->N) : 0;
+  w.route_scratch = rb ? static_cast<void*>(c.take<char>(rb)) : nullptr;
   if (out) *out = w;
   return c.off;
 }
@@ -160,9 +170,9 @@ int moe_max_rows(int T, int N, int K, int capacity, int capacity_group) {
   return r > INT_MAX ? INT_MAX : static_cast<int>(r);
 }
 
-size_t moe_route_workspace_size(int T, int N, int K) {
-  if (T <= 0 || N <= 0 || K <= 0) return 0;
-  return carve_count(nullptr, T, N, K, true, nullptr);
+size_t moe_route_workspace_size(int T, int d_model, int N, int K) {
+  if (T <= 0 || d_model <= 0 || N <= 0 || K <= 0) return 0;
+  return carve_count(nullptr, T, d_model, N, K, nullptr);
 }
 
 int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alpha, int dt,
@@ -181,13 +191,16 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   CountWs w{};
-  if (C_req) {
-    if (!workspace || workspace_bytes < moe_route_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
-    carve_count(workspace, T, N, K, true, &w);
+  const bool split =
+      route_split_slices(N, d_model, dt, logits_mode, logits_mode == 0 && w_shared_gate) > 0;
+  if (C_req || split) {
+    if (!workspace || workspace_bytes < moe_route_workspace_size(T, d_model, N, K))
+      return MOE_ERR_WORKSPACE;
+    carve_count(workspace, T, d_model, N, K, &w);
   }
   MOE_HIP(launch_route(T, d_model, N, K, score, renorm, alpha, dt, x, w_router, logit_bias,
                        expert_bias, logits_mode == 0 ? w_shared_gate : nullptr, logits,
-                       logits_mode, topk_idx, topk_r, s_tok, stream));
+                       logits_mode, topk_idx, topk_r, s_tok, w.route_scratch, stream));
   if (C_req) {
     MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
     MOE_HIP(launch_scan(T, N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, nullptr, stream));
@@ -197,7 +210,7 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
 
 size_t moe_permute_workspace_size(int T, int N, int K) {
   if (T <= 0 || N <= 0 || K <= 0) return 0;
-  return carve_count(nullptr, T, N, K, false, nullptr);
+  return carve_count(nullptr, T, -1, N, K, nullptr);
 }
 
 int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_group, int dt,
@@ -213,7 +226,7 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_gro
   if (T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_permute_workspace_size(T, N, K)) return MOE_ERR_WORKSPACE;
   CountWs w{};
-  carve_count(workspace, T, N, K, false, &w);
+  carve_count(workspace, T, -1, N, K, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
                       stream));
@@ -263,7 +276,7 @@ int moe_permute_noalloc(int T, int d_model, int N, int K, int capacity, int capa
   void* ws = device_scratch();
   if (ws == nullptr) return MOE_ERR_HIP;
   CountWs w{};
-  carve_count(ws, T, N, K, false, &w);
+  carve_count(ws, T, -1, N, K, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
                       stream));
@@ -507,7 +520,7 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   const int rows = moe_max_rows(T, N, K, a->capacity, a->capacity_group);
   MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
                        a->logit_bias, a->expert_bias, a->w_shared_gate, w.logits, 0, w.topk_idx,
-                       w.topk_r, w.s_tok, stream));
+                       w.topk_r, w.s_tok, w.route_scratch, stream));
   MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
   MOE_HIP(launch_scan(T, N, a->capacity, a->capacity_group, w.hist, w.C_req, w.C_keep,
                       w.offsets, a->count_accum, stream));

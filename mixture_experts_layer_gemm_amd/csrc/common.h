@@ -56,11 +56,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // launchers (enqueue only; return hipError_t of the launch)
 // ---------------------------------------------------------------------------------
 // expert_bias: selection-only bias b of auxiliary-loss-free balancing, or nullptr
+// scratch: route_scratch_bytes(T, d_model, N) bytes for the split-K logits of many experts
+// (route_split_slices > 0), else unused and may be nullptr
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
                         const float* expert_bias, const void* w_shared_gate, float* logits,
                         int logits_mode,
-                        int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream);
+                        int32_t* topk_idx, float* topk_r, float* s_tok, void* scratch,
+                        hipStream_t stream);
+int route_split_slices(int N, int d_model, int dt, int logits_mode, bool has_gate);
+size_t route_scratch_bytes(int T, int d_model, int N);
 
 hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
                         int32_t* loc_rank, hipStream_t stream);

@@ -21,7 +21,10 @@
 // Eq. 35): with a persistent expert bias b the keys become z + b (softmax rules) or
 // sigmoid(z) + b (sigmoid affinities), summed in fp32, while the coefficients are still
 // computed from the unbiased logits of the selected experts.
+#include <utility>
+
 #include "common.h"
+#include "gemm_common.h"
 
 using namespace moe;
 
@@ -204,17 +207,201 @@ __device__ void logits_f32(const float* __restrict__ x, const float* __restrict_
   }
 }
 
-template <int BT, int NBT, int WAVES, int U>
+// ---- phase 1 for many experts (128 < N <= 256, bf16): split-K logits ----------------
+// Each workgroup of 4 waves computes partial logits of LS_BT tokens x all N experts over
+// one of P equal slices of d_model; the route kernel then adds the P slices in a fixed
+// order. Wave w owns experts 64 w .. 64 w + 63 (two 32-row blocks of W_r, packed once per
+// call into the MFMA operand layout and loaded straight from global memory into
+// v_mfma_f32_32x32x16_bf16 A-operand registers, four stages ahead, 1 KB per load)
+// against all LS_BT tokens (x staged through a 4-stage LDS ring by direct-to-LDS loads,
+// XOR-swizzled chunks). Every W_r byte of a slice enters a compute unit once per 128
+// tokens instead of once per 32. Every stage issues the same loads (past the last stage
+// the last stage's addresses again), so one vmcnt wait per stage covers what it reads.
+constexpr int kRouteMaxSlices = 4;                   // d_model slices (partial logits)
+constexpr int LS_BT = 128;                           // tokens per workgroup
+constexpr int LS_BK = 64;                            // k per stage
+constexpr int LS_XS = 4;                             // x ring depth (stages)
+constexpr int LS_XSTAGE = LS_BT * LS_BK * 2;         // bytes per x stage
+constexpr int LS_XDPW = LS_XSTAGE / (1024 * 4);      // direct-to-LDS loads per wave per stage
+constexpr int LS_WPS = 2 * (LS_BK / 16);             // W_r loads per wave per stage
+constexpr int LS_PER = LS_XDPW + LS_WPS;
+constexpr int LS_RS = 4;                             // W_r stages in flight
+// ops issued after the W_r (resp. x) loads of stage s when stage s begins
+constexpr int LS_WAITN = (LS_RS - 1) * LS_PER < LS_WPS + (LS_XS - 2) * LS_PER
+                             ? (LS_RS - 1) * LS_PER : LS_WPS + (LS_XS - 2) * LS_PER;
+static_assert(LS_WAITN <= 63, "vmcnt range");
+
+__device__ __forceinline__ int ls_swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+// (non-temporal: x is read once, so it should not push W_r out of L2)
+__device__ __forceinline__ void ls_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+// 16-byte load into registers the compiler does not track (read after the stage wait)
+template <int OFF>
+__device__ __forceinline__ void ls_ldg16(u32x4& dst, const void* sbase, uint32_t voff) {
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3"
+               : "=v"(dst)
+               : "v"(voff), "s"(sbase), "i"(OFF)
+               : "memory");
+}
+template <typename F, int... I>
+__device__ __forceinline__ void ls_unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void ls_unroll(F&& f) {
+  ls_unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// grid (ceil(T / LS_BT), P); part[p][t][n] = sum over slice p of x[t][k] W_r[n][k];
+// N a multiple of 64, kslice = d / P a multiple of LS_RS LS_BK; wpk is W_r in the
+// moe_pack_weights layout (the A operand of v_mfma_f32_32x32x16_bf16, 1 KB per 32 rows
+// x 16 k, contiguous along k for each 32-row block)
+__global__ void __launch_bounds__(256, 1)
+logits_split_kernel(int T, int d, int N, int kslice, const uint16_t* __restrict__ x,
+                    const uint16_t* __restrict__ wpk, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char lds[LS_XS * LS_XSTAGE];
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * LS_BT;
+  const int kp = blockIdx.y;
+  const int nst = kslice / LS_BK;
+  const uint32_t lds_base = static_cast<uint32_t>((size_t)((lds_char*)lds));
+  const uint32_t rowb = static_cast<uint32_t>(d) * 2u;
+  const char* xs0 = reinterpret_cast<const char*>(x) + static_cast<size_t>(kp) * kslice * 2;
+  // this slice's first 16-wide k step within each packed 32-row block
+  const char* ws0 = reinterpret_cast<const char*>(wpk) + static_cast<size_t>(kp) * (kslice / 16) * 1024;
+  // x: load i of wave w brings tile rows 8 (4 i + w) .. + 7, lane j row 8 (4 i + w) + (j >> 3),
+  // physical chunk j & 7 (rows past T repeat row T - 1)
+  uint32_t xo[LS_XDPW];
+#pragma unroll
+  for (int i = 0; i < LS_XDPW; ++i) {
+    const int row = (4 * i + wv) * 8 + (lane >> 3);
+    xo[i] = static_cast<uint32_t>(min(t0 + row, T - 1)) * rowb +
+            static_cast<uint32_t>(ls_swz(row, lane & 7) << 4);
+  }
+  // W_r: block b of this wave is packed 32-row block 2 w + b (past N: the last block,
+  // computed and never stored); each k16 step of a block is 1 KB, 16 bytes per lane
+  uint32_t wo[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    wo[b] = static_cast<uint32_t>(min(2 * wv + b, N / 32 - 1)) * 32u * rowb +
+            static_cast<uint32_t>(lane) * 16u;
+  // LDS byte offset of this lane's x fragment for k16 step u (token block 0)
+  uint32_t xoff[LS_BK / 16];
+#pragma unroll
+  for (int u = 0; u < LS_BK / 16; ++u)
+    xoff[u] = static_cast<uint32_t>(lr * (LS_BK * 2) + (ls_swz(lr, 2 * u + lh) << 4));
+
+  auto issue_x = [&](int ks, int slot) {
+    const char* sb = xs0 + static_cast<size_t>(ks) * (LS_BK * 2);
+    const uint32_t dst = lds_base + slot * LS_XSTAGE + wv * 1024;
+#pragma unroll
+    for (int i = 0; i < LS_XDPW; ++i) ls_dma16(xo[i], sb, dst + i * 4096);
+  };
+  u32x4 wrg[LS_RS][LS_BK / 16][2];
+  auto issue_w = [&](u32x4 (&dst)[LS_BK / 16][2], int ks, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const char* sb = ws0 + static_cast<size_t>(ks) * ((LS_BK / 16) * 1024);
+    ls_ldg16<u * 1024>(dst[u][0], sb, wo[0]);
+    ls_ldg16<u * 1024>(dst[u][1], sb, wo[1]);
+  };
+  // prologue: the loads of virtual stages -V..-1 (targets clamped to the last stage), in
+  // the order a steady stage issues them
+  constexpr int V = (LS_XS - 1) > LS_RS ? (LS_XS - 1) : LS_RS;
+  ls_unroll<V>([&](auto vc) {
+    constexpr int v = decltype(vc)::value - V;
+    constexpr int xs_t = v + LS_XS - 1;
+    if constexpr (xs_t >= 0) issue_x(min(xs_t, nst - 1), xs_t);
+    constexpr int ws_t = v + LS_RS;
+    if constexpr (ws_t >= 0) {
+      const int ks = min(ws_t, nst - 1);
+      ls_unroll<LS_BK / 16>([&](auto uc) { issue_w(wrg[ws_t], ks, uc); });
+    }
+  });
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][j][v] = 0.f;
+
+  for (int s0 = 0; s0 < nst; s0 += LS_RS) {
+    ls_unroll<LS_RS>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const int s = s0 + r;
+      wait_vmcnt<LS_WAITN>();
+      __syncthreads();
+      // past the end: the last stage again (loaded, never read)
+      issue_x(min(s + LS_XS - 1, nst - 1), (s + LS_XS - 1) % LS_XS);
+      const int ts = min(s + LS_RS, nst - 1);
+      const char* xt = lds + (s % LS_XS) * LS_XSTAGE;
+      bf16x8 xv[2][4];
+      auto xread = [&](int u, bf16x8* v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[j] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(xt + xoff[u] + j * (32 * LS_BK * 2)));
+      };
+      xread(0, xv[0]);
+      ls_unroll<LS_BK / 16>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + 1 < LS_BK / 16) xread(u + 1, xv[(u + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            acc[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, wrg[r][u][b]), xv[u & 1][j], acc[b][j], 0, 0, 0);
+        issue_w(wrg[r], ts, uc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  }
+  wait_vmcnt<0>();  // no load may land after the workgroup ends
+  // lane (lr, lh) holds token 32 j + lr, experts 64 w + 32 b + 8 q + 4 lh + {0..3}. N is a
+  // multiple of 64, so a wave's experts are all real or (past N) all absent: absent ones
+  // store nothing (their rows would land in the next token's)
+  if (64 * wv >= N) return;
+  float* pp = part + static_cast<size_t>(kp) * T * N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 32 * j + lr;
+    if (t >= T) continue;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = 64 * wv + 32 * b + 8 * q + 4 * lh;
+        *reinterpret_cast<floatx4*>(pp + static_cast<size_t>(t) * N + n) =
+            floatx4{acc[b][j][4 * q], acc[b][j][4 * q + 1], acc[b][j][4 * q + 2],
+                    acc[b][j][4 * q + 3]};
+      }
+  }
+}
+
+// TILE_ONLY: logits come from memory (logits_mode 1 or 2), so LDS holds the one final
+// tile instead of a partial tile per wave
+template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false>
 __global__ void __launch_bounds__(WAVES * 64)
 route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
              const void* __restrict__ x, const void* __restrict__ w_router,
              const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
              const void* __restrict__ w_gate_vec,
              float* __restrict__ logits, int logits_mode, int32_t* __restrict__ topk_idx,
-             float* __restrict__ topk_r, float* __restrict__ s_tok) {
+             float* __restrict__ topk_r, float* __restrict__ s_tok,
+             const float* __restrict__ part, int nparts) {
   constexpr int THREADS = WAVES * 64;
   constexpr int ldz = NBT * 16 + 1;
-  __shared__ float smem[WAVES * BT * ldz];  // bf16 path: one partial tile per wave
+  __shared__ float smem[(TILE_ONLY ? 1 : WAVES) * BT * ldz];  // bf16 path: a partial tile per wave
   float* z = smem;  // final logits tile [BT][ldz]
   const int t0 = blockIdx.x * BT;
   const int tid = threadIdx.x;
@@ -226,6 +413,38 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
       const int t = i / N, n = i % N;
       if (t0 + t < T) z[t * ldz + n] = logits[static_cast<size_t>(t0 + t) * N + n];
     }
+  } else if (logits_mode == 2) {
+    // the split-K slices of logits_split_kernel, added in slice order, then the bias; a
+    // thread's loads for EPT elements of every slice are all issued before any sum
+    constexpr int EPT = 8;
+    const size_t slice = static_cast<size_t>(T) * N;
+    for (int i0 = tid; i0 < BT * N; i0 += THREADS * EPT) {
+      float pv[kRouteMaxSlices][EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = i0 + e * THREADS;
+        const bool ok = i < BT * N && t0 + i / N < T;
+        const size_t o = ok ? static_cast<size_t>(t0) * N + i : 0;
+#pragma unroll
+        for (int q = 0; q < kRouteMaxSlices; ++q)
+          pv[q][e] = (ok && q < nparts) ? part[q * slice + o] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = i0 + e * THREADS;
+        if (i < BT * N && t0 + i / N < T) {
+          const int t = i / N, n = i % N;
+          float v = pv[0][e];
+#pragma unroll
+          for (int q = 1; q < kRouteMaxSlices; ++q)
+            if (q < nparts) v += pv[q][e];
+          if (logit_bias != nullptr) v += logit_bias[n];
+          z[t * ldz + n] = v;
+        }
+      }
+    }
+  } else if (TILE_ONLY) {
+    return;  // not launched for logits computed here
   } else if (dt == 1) {
     const int NB = (ncol + 15) / 16;
     logits_bf16<BT, NBT, WAVES, U>(static_cast<const uint16_t*>(x),
@@ -252,7 +471,7 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
   __syncthreads();
 
-  if (logits_mode == 0 && logits != nullptr) {
+  if (logits_mode != 1 && logits != nullptr) {
     for (int i = tid; i < BT * N; i += THREADS) {
       const int t = i / N, n = i % N;
       if (t0 + t < T) logits[static_cast<size_t>(t0 + t) * N + n] = z[t * ldz + n];
@@ -337,27 +556,67 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
 }
 
-template <int BT, int NBT, int WAVES, int U>
+template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false>
 hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
                       const void* x, const void* w_router, const float* logit_bias,
                       const float* sel_bias, const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
-                      float* topk_r, float* s_tok, hipStream_t stream) {
+                      float* topk_r, float* s_tok, const float* part, int nparts,
+                      hipStream_t stream) {
   const int grid = (T + BT - 1) / BT;
-  hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U>), dim3(grid), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U, TILE_ONLY>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, sel_bias,
                      w_gate_vec,
-                     logits, logits_mode, topk_idx, topk_r, s_tok);
+                     logits, logits_mode, topk_idx, topk_r, s_tok, part, nparts);
   return hipGetLastError();
 }
+
+}  // namespace
+
+// d_model slices of the split-K logits for this router, or 0 when the fused single-pass
+// router runs (few experts, fp32, a shared-gate column, or logits given as input)
+int route_split_slices(int N, int d_model, int dt, int logits_mode, bool has_gate) {
+  if (logits_mode != 0 || dt != 1 || has_gate || N <= 128 || N > 256 || N % 64 != 0) return 0;
+  // up to 4 slices: 256 workgroups of 128 tokens at 8192 tokens
+  for (int P = kRouteMaxSlices; P >= 1; P >>= 1)
+    if (d_model % (P * LS_RS * LS_BK) == 0) return P;
+  return 0;
+}
+
+// scratch of the split-K path: the partial logit slices, then W_r packed (256-byte aligned)
+size_t route_scratch_bytes(int T, int d_model, int N) {
+  if (N <= 128) return 0;
+  const size_t part = (static_cast<size_t>(kRouteMaxSlices) * T * N * sizeof(float) + 255) / 256 * 256;
+  return part + static_cast<size_t>(N) * d_model * 2;
+}
+
+namespace {
 
 }  // namespace
 
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
                         const float* expert_bias, const void* w_shared_gate, float* logits, int logits_mode,
-                        int32_t* topk_idx, float* topk_r, float* s_tok, hipStream_t stream) {
+                        int32_t* topk_idx, float* topk_r, float* s_tok, void* scratch,
+                        hipStream_t stream) {
   const int ncol = N + ((w_shared_gate != nullptr && logits_mode == 0) ? 1 : 0);
   const int NB = (ncol + 15) / 16;
+  const int P = route_split_slices(N, d_model, dt, logits_mode, w_shared_gate != nullptr);
+  if (P > 0) {  // pack W_r, split-K logits into slices, top-K over their fixed-order sum
+    if (scratch == nullptr) return hipErrorInvalidValue;
+    float* partials = static_cast<float*>(scratch);
+    char* wpk = static_cast<char*>(scratch) +
+                (static_cast<size_t>(kRouteMaxSlices) * T * N * sizeof(float) + 255) / 256 * 256;
+    hipError_t e = launch_pack_weights(1, N, d_model, w_router, wpk, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(logits_split_kernel, dim3((T + LS_BT - 1) / LS_BT, P), dim3(256), 0,
+                       stream, T, d_model, N, d_model / P, static_cast<const uint16_t*>(x),
+                       reinterpret_cast<const uint16_t*>(wpk), partials);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_cfg<32, 17, 8, 1, true>(T, d_model, N, K, score, renorm, alpha, dt, nullptr,
+                                          nullptr, logit_bias, expert_bias, nullptr, logits, 2,
+                                          topk_idx, topk_r, nullptr, partials, P, stream);
+  }
   // (tokens per workgroup, column blocks, waves, k steps in flight per wave): small N
   // uses 16 tokens and 8 waves; large N 32 tokens (router rows re-read half as often)
 #define MOE_ROUTE_CASE(BT_, NBT_, W_, U_)                                                    \
@@ -365,7 +624,7 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
     return launch_cfg<BT_, NBT_, W_, U_>(T, d_model, N, K, score, renorm, alpha, dt, x,      \
                                          w_router, logit_bias, expert_bias, w_shared_gate,   \
                                          logits, logits_mode, topk_idx, topk_r, s_tok,       \
-                                         stream);
+                                         nullptr, 0, stream);
   MOE_ROUTE_CASE(16, 1, 8, 8)
   MOE_ROUTE_CASE(16, 2, 8, 8)
   MOE_ROUTE_CASE(16, 4, 8, 4)

@@ -69,7 +69,7 @@ def _load() -> ctypes.CDLL:
         "moe_capacity_from_factor": (I, [c_double, I, I, I]),
         "moe_rank_capacity_from_factor": (I, [c_double, I, I]),
         "moe_max_rows": (I, [I, I, I, I, I]),
-        "moe_route_workspace_size": (S, [I, I, I]),
+        "moe_route_workspace_size": (S, [I, I, I, I]),
         "moe_route": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_bias_update": (I, [I, F, P, P, I, P]),
         "moe_pack_weights_transposed": (I, [I, I, I, I, I, P, P, P, P]),
@@ -175,7 +175,7 @@ def moe_route(x, w_router, K: int, score: int = SCORE_SOFTMAX, renorm: bool = Tr
                       if (w_shared_gate is not None and logits_mode == 0) else None),
                C_req=torch.empty(N, dtype=torch.int32, device=dev) if want_counts else None,
                logits=logits)
-    ws = _workspace(lib.moe_route_workspace_size(T, N, K), dev)
+    ws = _workspace(lib.moe_route_workspace_size(T, d, N, K), dev)
     st = lib.moe_route(T, d, N, K, score, int(renorm), float(alpha), dt,
                        None if logits_mode == 1 else _ptr(x),
                        None if logits_mode == 1 else _ptr(w_router),

@@ -128,6 +128,13 @@ SMALL = {
                                K=4, d_r=512, shared_widths=(256,), score=SCORE_SIGMOID,
                                alpha=2.5, capacity_factor=0.75, capacity_group=2,
                                zipf_bias=True, std_w=0.04),
+    # fine-grained routing at a small size: 256 experts, top-8 of sigmoid affinities, a
+    # ragged last token tile (the split-K router logits of many experts)
+    "S_wide": Config("small-256-experts", 23, T=1000, d_model=1024, N=256, K=8, d_r=256,
+                     shared_widths=(128,), score=SCORE_SIGMOID, alpha=2.5, std_w=0.03),
+    # 192 experts (three groups of 64) under the Olmo rule, d_model in two slices
+    "S_wide192": Config("small-192-experts", 24, T=300, d_model=768, N=192, K=6, d_r=128,
+                        shared_widths=(64,), alpha=6.0, std_w=0.04),
 }
 
 

@@ -60,8 +60,8 @@ def test_rank_capacity_matches_eq23(c, K, T_s):
 
 
 def test_workspace_sizes_are_positive_and_monotone():
-    a = moe.lib.moe_route_workspace_size(4096, 64, 4)
-    b = moe.lib.moe_route_workspace_size(8192, 64, 4)
+    a = moe.lib.moe_route_workspace_size(4096, 2048, 64, 4)
+    b = moe.lib.moe_route_workspace_size(8192, 2048, 64, 4)
     assert 0 < a < b
     assert moe.lib.moe_permute_workspace_size(0, 64, 4) == 0
     args = moe.ForwardArgs()
@@ -97,7 +97,17 @@ def test_route_rejects_bad_arguments_without_launching():
     assert _route(gate=1) == moe.MOE_ERR_INVALID_ARG          # gate needs s_tok
     assert _route(mode=1) == moe.MOE_ERR_INVALID_ARG          # mode 1 needs logits
     assert _route(creq=1, ws=None) == moe.MOE_ERR_WORKSPACE
+    # bf16 logits of more than 128 experts run split over d_model from a packed router copy
+    # in the workspace: required even without C_req (and not for fp32 or a gate column)
+    assert _route(T=64, d=1024, N=256, K=8, ws=None) == moe.MOE_ERR_WORKSPACE
     assert _route(T=0) == moe.MOE_OK                          # empty input: nothing to do
+
+
+def test_route_workspace_holds_split_logits_and_packed_router():
+    T, d, N, K = 8192, 7168, 256, 8
+    need = 4 * T * N * 4 + N * d * 2                           # 4 partial slices + packed W_r
+    assert moe.lib.moe_route_workspace_size(T, d, N, K) >= need
+    assert moe.lib.moe_route_workspace_size(T, d, 128, K) < need // 4   # fused router: no slices
 
 
 def test_permute_grouped_combine_forward_reject_bad_arguments():
