@@ -39,7 +39,25 @@ def test_persistent_gemm_has_no_untracked_load_hazard(tmp_path):
 
 
 @pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None, reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["gemm_stream.hip", "gemm.hip", "gemm_packed.hip", "backward.hip"])
+def test_split_router_logits_have_no_untracked_load_hazard(tmp_path):
+    """The split-K router logits (many experts) load the packed router rows into registers
+    from inline asm and the token rows into LDS, with one explicit wait per stage: four
+    stages of router rows and three of token rows ahead, 12 loads a stage, so the wait
+    allows 32 later loads; the stage loop is unrolled four times."""
+    asm = compile_to_asm(os.path.join(CSRC, "route.hip"), os.path.join(ROOT, "include"),
+                         str(tmp_path / "route.s"))
+    bodies = kernel_bodies(asm, "logits_split_kernel")
+    assert len(bodies) == 1, sorted(bodies)
+    for name, body in bodies.items():
+        assert "scratch_" not in body, f"{name} spills to scratch"
+        hz = untracked_load_hazards(body)
+        assert not hz, f"{name}: {hz[:3]}"
+        assert body.count("s_waitcnt vmcnt(32)") == 4, name
+
+
+@pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None, reason="hipcc not installed")
+@pytest.mark.parametrize("src", ["gemm_stream.hip", "gemm.hip", "gemm_packed.hip", "backward.hip",
+                                 "route.hip"])
 def test_m0_is_only_set_for_direct_to_lds_loads(src, tmp_path):
     """The direct-to-LDS loads set M0 in inline asm and list it as clobbered. M0 is a
     reserved register the compiler does not preserve around such asm, so that is only
