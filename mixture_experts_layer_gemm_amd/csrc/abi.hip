@@ -28,6 +28,7 @@ struct Carver {
 };
 
 int nchunks_of(int T) { return (T + moe::kChunk - 1) / moe::kChunk; }
+int rows_of(int T, int R) { return (T + R - 1) / R; }
 
 int check_router_dims(int T, int d_model, int N, int K) {
   if (T < 0 || d_model <= 0 || N <= 0 || K <= 0 || K > N) return MOE_ERR_INVALID_ARG;
@@ -67,12 +68,13 @@ struct CountWs {
   void* route_scratch;  // split-K logits of many experts (moe_route only)
 };
 
-// d_model < 0: no route scratch (moe_permute)
+// d_model < 0: no route scratch (moe_permute, histogram rows of kChunk tokens); else the
+// router counts in its epilogue, in rows of 16 or 32 tokens (sized for 16)
 size_t carve_count(void* ws, int T, int d_model, int N, int K, CountWs* out) {
   Carver c(ws);
   CountWs w;
   const bool route = d_model >= 0;
-  w.hist = c.take<int32_t>(static_cast<size_t>(nchunks_of(T)) * N);
+  w.hist = c.take<int32_t>(static_cast<size_t>(route ? rows_of(T, 16) : nchunks_of(T)) * N);
   w.loc_rank = c.take<int32_t>(static_cast<size_t>(T) * K);
   w.c_keep = route ? c.take<int32_t>(N) : nullptr;
   w.offsets = route ? c.take<int32_t>(N + 1) : nullptr;
@@ -104,7 +106,7 @@ size_t carve_forward(const moe_forward_args* a, void* ws, FwdWs* out) {
   w.topk_idx = a->topk_idx ? a->topk_idx : c.take<int32_t>(T * K);
   w.topk_r = a->topk_r ? a->topk_r : c.take<float>(T * K);
   w.s_tok = !gate ? nullptr : (a->s_tok ? a->s_tok : c.take<float>(T));
-  w.hist = c.take<int32_t>(static_cast<size_t>(nchunks_of(a->T)) * N);
+  w.hist = c.take<int32_t>(static_cast<size_t>(rows_of(a->T, 16)) * N);  // router rows
   w.loc_rank = c.take<int32_t>(T * K);
   w.C_req = a->C_req ? a->C_req : c.take<int32_t>(N);
   w.C_keep = a->C_keep ? a->C_keep : c.take<int32_t>(N);
@@ -198,12 +200,15 @@ int moe_route(int T, int d_model, int N, int K, int score, int renorm, float alp
       return MOE_ERR_WORKSPACE;
     carve_count(workspace, T, d_model, N, K, &w);
   }
+  const void* gate = logits_mode == 0 ? w_shared_gate : nullptr;
   MOE_HIP(launch_route(T, d_model, N, K, score, renorm, alpha, dt, x, w_router, logit_bias,
-                       expert_bias, logits_mode == 0 ? w_shared_gate : nullptr, logits,
-                       logits_mode, topk_idx, topk_r, s_tok, w.route_scratch, stream));
-  if (C_req) {
-    MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-    MOE_HIP(launch_scan(T, N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, nullptr, stream));
+                       expert_bias, gate, logits, logits_mode, topk_idx, topk_r, s_tok,
+                       w.route_scratch, C_req ? w.hist : nullptr, C_req ? w.loc_rank : nullptr,
+                       stream));
+  if (C_req) {  // the router counted its tiles; the per-expert sums of those rows
+    const int R = route_tile_tokens(N, d_model, dt, logits_mode, gate != nullptr);
+    MOE_HIP(launch_scan(rows_of(T, R), N, -1, 0, w.hist, C_req, w.c_keep, w.offsets, nullptr,
+                        stream));
   }
   return MOE_OK;
 }
@@ -228,10 +233,9 @@ int moe_permute(int T, int d_model, int N, int K, int capacity, int capacity_gro
   CountWs w{};
   carve_count(workspace, T, -1, N, K, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
-                      stream));
-  MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
-                         dest_row, row_token, x_perm, stream));
+  MOE_HIP(launch_place(T, d_model, N, K, moe::kChunk, capacity, capacity_group, dt, x, topk_idx,
+                       w.hist, w.loc_rank, C_req, C_keep, offsets, nullptr, dest_row, row_token,
+                       x_perm, stream));
   return MOE_OK;
 }
 
@@ -278,10 +282,9 @@ int moe_permute_noalloc(int T, int d_model, int N, int K, int capacity, int capa
   CountWs w{};
   carve_count(ws, T, -1, N, K, &w);
   MOE_HIP(launch_count(T, N, K, topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, capacity, capacity_group, w.hist, C_req, C_keep, offsets, nullptr,
-                      stream));
-  MOE_HIP(launch_scatter(T, d_model, N, K, dt, x, topk_idx, w.hist, w.loc_rank, C_keep, offsets,
-                         dest_row, row_token, x_perm, stream));
+  MOE_HIP(launch_place(T, d_model, N, K, moe::kChunk, capacity, capacity_group, dt, x, topk_idx,
+                       w.hist, w.loc_rank, C_req, C_keep, offsets, nullptr, dest_row, row_token,
+                       x_perm, stream));
   return MOE_OK;
 }
 
@@ -518,14 +521,15 @@ int moe_forward(const moe_forward_args* a, void* workspace, size_t workspace_byt
   carve_forward(a, workspace, &w);
   const int T = a->T, d = a->d_model, N = a->N, K = a->K;
   const int rows = moe_max_rows(T, N, K, a->capacity, a->capacity_group);
+  // the router also counts its tiles; placement then needs one launch (two past
+  // place_fused's histogram size)
   MOE_HIP(launch_route(T, d, N, K, a->score, a->renorm, a->alpha, a->dt, a->x, a->w_router,
                        a->logit_bias, a->expert_bias, a->w_shared_gate, w.logits, 0, w.topk_idx,
-                       w.topk_r, w.s_tok, w.route_scratch, stream));
-  MOE_HIP(launch_count(T, N, K, w.topk_idx, w.hist, w.loc_rank, stream));
-  MOE_HIP(launch_scan(T, N, a->capacity, a->capacity_group, w.hist, w.C_req, w.C_keep,
-                      w.offsets, a->count_accum, stream));
-  MOE_HIP(launch_scatter(T, d, N, K, a->dt, a->x, w.topk_idx, w.hist, w.loc_rank, w.C_keep,
-                         w.offsets, w.dest_row, w.row_token, w.x_perm, stream));
+                       w.topk_r, w.s_tok, w.route_scratch, w.hist, w.loc_rank, stream));
+  const int R = route_tile_tokens(N, d, a->dt, 0, a->w_shared_gate != nullptr);
+  MOE_HIP(launch_place(T, d, N, K, R, a->capacity, a->capacity_group, a->dt, a->x, w.topk_idx,
+                       w.hist, w.loc_rank, w.C_req, w.C_keep, w.offsets, a->count_accum,
+                       w.dest_row, w.row_token, w.x_perm, stream));
   MOE_HIP(expert_passes(N, d, a->d_r, a->d_s, a->dt, a->weights_packed == 1, a->x, T,
                         w.row_token, w.offsets, rows, a->w_gate, a->w_up, a->w_down, a->ws_gate,
                         a->ws_up, a->ws_down, w.h_perm, w.f_perm, w.h_shared, w.g, 0, stream));

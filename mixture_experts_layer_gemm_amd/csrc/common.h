@@ -58,31 +58,48 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // expert_bias: selection-only bias b of auxiliary-loss-free balancing, or nullptr
 // scratch: route_scratch_bytes(T, d_model, N) bytes for the split-K logits of many experts
 // (route_split_slices > 0), else unused and may be nullptr
+// hist, loc_rank (or nullptr): the router also counts its selections, one histogram row
+// of N counts per workgroup of route_tile_tokens(...) tokens and each route's rank among
+// its row's routes to the same expert (the input of launch_place with that R)
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
                         const float* expert_bias, const void* w_shared_gate, float* logits,
                         int logits_mode,
                         int32_t* topk_idx, float* topk_r, float* s_tok, void* scratch,
-                        hipStream_t stream);
+                        int32_t* hist, int32_t* loc_rank, hipStream_t stream);
 int route_split_slices(int N, int d_model, int dt, int logits_mode, bool has_gate);
 size_t route_scratch_bytes(int T, int d_model, int N);
+int route_tile_tokens(int N, int d_model, int dt, int logits_mode, bool has_gate);
 
+// histogram rows of kChunk tokens from given selections
 hipError_t launch_count(int T, int N, int K, const int32_t* topk_idx, int32_t* hist,
                         int32_t* loc_rank, hipStream_t stream);
 
 // capacity < 0: keep every route; group == 0: per-expert limit; group > 0: one budget
 // `capacity` shared by each run of `group` consecutive experts. count_accum (or nullptr)
-// gets C_req added (feedback-window counts of the bias controller).
-hipError_t launch_scan(int T, int N, int capacity, int group, int32_t* hist, int32_t* C_req,
-                       int32_t* C_keep, int32_t* offsets, int32_t* count_accum,
+// gets C_req added (feedback-window counts of the bias controller). hist (nrows x N) is
+// overwritten with each row's base ranks.
+hipError_t launch_scan(int nrows, int N, int capacity, int group, int32_t* hist,
+                       int32_t* C_req, int32_t* C_keep, int32_t* offsets, int32_t* count_accum,
                        hipStream_t stream);
+
+// From histogram rows of R tokens (R in {16, 32, 64}): C_req, C_keep, offsets, the
+// restoration map and, when x_perm != nullptr, the packed row copy. One launch while
+// place_fused(T, N, R), else scan then map / scatter (hist overwritten).
+bool place_fused(int T, int N, int R);
+hipError_t launch_place(int T, int d_model, int N, int K, int R, int capacity, int group,
+                        int dt, const void* x, const int32_t* topk_idx, int32_t* hist,
+                        const int32_t* loc_rank, int32_t* C_req, int32_t* C_keep,
+                        int32_t* offsets, int32_t* count_accum, int32_t* dest_row,
+                        int32_t* row_token, void* x_perm, hipStream_t stream);
 
 // b_i += gamma sign(sum_j C_j - N C_i); C zeroed when reset != 0
 hipError_t launch_bias_update(int N, float gamma, int32_t* count_accum, float* expert_bias,
                               int reset, hipStream_t stream);
 
-// x_perm == nullptr: restoration map only (no row copy)
-hipError_t launch_scatter(int T, int d_model, int N, int K, int dt, const void* x,
+// x_perm == nullptr: restoration map only (no row copy); hist_base: base ranks of rows
+// of R tokens (launch_scan's output)
+hipError_t launch_scatter(int T, int d_model, int N, int K, int R, int dt, const void* x,
                           const int32_t* topk_idx, const int32_t* hist_base,
                           const int32_t* loc_rank, const int32_t* C_keep,
                           const int32_t* offsets, int32_t* dest_row, int32_t* row_token,

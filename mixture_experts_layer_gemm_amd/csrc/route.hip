@@ -398,8 +398,10 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
              const void* __restrict__ w_gate_vec,
              float* __restrict__ logits, int logits_mode, int32_t* __restrict__ topk_idx,
              float* __restrict__ topk_r, float* __restrict__ s_tok,
-             const float* __restrict__ part, int nparts) {
+             const float* __restrict__ part, int nparts, int32_t* __restrict__ hist,
+             int32_t* __restrict__ loc_rank) {
   constexpr int THREADS = WAVES * 64;
+  static_assert(BT <= 32, "one 32-bit token mask per expert");
   constexpr int ldz = NBT * 16 + 1;
   __shared__ float smem[(TILE_ONLY ? 1 : WAVES) * BT * ldz];  // bf16 path: a partial tile per wave
   float* z = smem;  // final logits tile [BT][ldz]
@@ -407,6 +409,11 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   const int tid = threadIdx.x;
   const bool has_gate = (w_gate_vec != nullptr) && logits_mode == 0;
   const int ncol = N + (has_gate ? 1 : 0);
+  // the tile's count (hist != nullptr): a 32-bit token mask per expert, OR-ed in LDS
+  __shared__ uint32_t s_mask[kMaxN];
+  __shared__ int s_tsel[BT][kMaxK];
+  if (hist != nullptr)
+    for (int i = tid; i < kMaxN; i += THREADS) s_mask[i] = 0u;
 
   if (logits_mode == 1) {
     for (int i = tid; i < BT * N; i += THREADS) {
@@ -551,8 +558,24 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
     if (act) {
       topk_idx[static_cast<size_t>(tok) * K + lane] = sele;
       topk_r[static_cast<size_t>(tok) * K + lane] = r;
+      if (hist != nullptr) s_tsel[t][lane] = sele;
     }
     if (has_gate && s_tok != nullptr && lane == 0) s_tok[tok] = sigmoid_f(zr[N]);
+  }
+  // ---- epilogue: this tile's histogram row and each route's rank within the row ------
+  // (the K experts of a token are distinct, so each token sets one bit per expert; OR is
+  // order-free and the rank is the popcount of the mask below the token)
+  if (hist != nullptr) {
+    const int nt = min(BT, T - t0);
+    __syncthreads();
+    for (int i = tid; i < nt * K; i += THREADS) atomicOr(&s_mask[s_tsel[i / K][i % K]], 1u << (i / K));
+    __syncthreads();
+    for (int i = tid; i < nt * K; i += THREADS) {
+      const int t = i / K;
+      loc_rank[static_cast<size_t>(t0) * K + i] = __popc(s_mask[s_tsel[t][i % K]] & ((1u << t) - 1u));
+    }
+    for (int e = tid; e < N; e += THREADS)
+      hist[static_cast<size_t>(blockIdx.x) * N + e] = __popc(s_mask[e]);
   }
 }
 
@@ -561,12 +584,12 @@ hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float a
                       const void* x, const void* w_router, const float* logit_bias,
                       const float* sel_bias, const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
                       float* topk_r, float* s_tok, const float* part, int nparts,
-                      hipStream_t stream) {
+                      int32_t* hist, int32_t* loc_rank, hipStream_t stream) {
   const int grid = (T + BT - 1) / BT;
   hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U, TILE_ONLY>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, sel_bias,
                      w_gate_vec,
-                     logits, logits_mode, topk_idx, topk_r, s_tok, part, nparts);
+                     logits, logits_mode, topk_idx, topk_r, s_tok, part, nparts, hist, loc_rank);
   return hipGetLastError();
 }
 
@@ -593,11 +616,18 @@ namespace {
 
 }  // namespace
 
+// tokens per router workgroup, i.e. per histogram row of the router's own count
+int route_tile_tokens(int N, int d_model, int dt, int logits_mode, bool has_gate) {
+  if (route_split_slices(N, d_model, dt, logits_mode, has_gate) > 0) return 32;
+  const int ncol = N + ((has_gate && logits_mode == 0) ? 1 : 0);
+  return (ncol + 15) / 16 <= 8 ? 16 : 32;
+}
+
 hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm, float alpha,
                         int dt, const void* x, const void* w_router, const float* logit_bias,
                         const float* expert_bias, const void* w_shared_gate, float* logits, int logits_mode,
                         int32_t* topk_idx, float* topk_r, float* s_tok, void* scratch,
-                        hipStream_t stream) {
+                        int32_t* hist, int32_t* loc_rank, hipStream_t stream) {
   const int ncol = N + ((w_shared_gate != nullptr && logits_mode == 0) ? 1 : 0);
   const int NB = (ncol + 15) / 16;
   const int P = route_split_slices(N, d_model, dt, logits_mode, w_shared_gate != nullptr);
@@ -615,7 +645,8 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
     if (e != hipSuccess) return e;
     return launch_cfg<32, 17, 8, 1, true>(T, d_model, N, K, score, renorm, alpha, dt, nullptr,
                                           nullptr, logit_bias, expert_bias, nullptr, logits, 2,
-                                          topk_idx, topk_r, nullptr, partials, P, stream);
+                                          topk_idx, topk_r, nullptr, partials, P, hist, loc_rank,
+                                          stream);
   }
   // (tokens per workgroup, column blocks, waves, k steps in flight per wave): small N
   // uses 16 tokens and 8 waves; large N 32 tokens (router rows re-read half as often)
@@ -624,7 +655,7 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
     return launch_cfg<BT_, NBT_, W_, U_>(T, d_model, N, K, score, renorm, alpha, dt, x,      \
                                          w_router, logit_bias, expert_bias, w_shared_gate,   \
                                          logits, logits_mode, topk_idx, topk_r, s_tok,       \
-                                         nullptr, 0, stream);
+                                         nullptr, 0, hist, loc_rank, stream);
   MOE_ROUTE_CASE(16, 1, 8, 8)
   MOE_ROUTE_CASE(16, 2, 8, 8)
   MOE_ROUTE_CASE(16, 4, 8, 4)

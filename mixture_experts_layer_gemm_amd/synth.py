@@ -130,6 +130,11 @@ SMALL = {
                                zipf_bias=True, std_w=0.04),
     # fine-grained routing at a small size: 256 experts, top-8 of sigmoid affinities, a
     # ragged last token tile (the split-K router logits of many experts)
+    # many tokens, Zipf-skewed and at capacity: the router's 16-token histogram rows
+    # (1025 x 64 counts) exceed what one placement workgroup re-reads, so the forward
+    # places with a scan, then the map
+    "S_longT": Config("small-many-tokens", 25, T=16400, d_model=256, N=64, K=4, d_r=128,
+                      shared_widths=(64,), capacity_factor=1.0, zipf_bias=True, std_w=0.05),
     "S_wide": Config("small-256-experts", 23, T=1000, d_model=1024, N=256, K=8, d_r=256,
                      shared_widths=(128,), score=SCORE_SIGMOID, alpha=2.5, std_w=0.03),
     # 192 experts (three groups of 64) under the Olmo rule, d_model in two slices

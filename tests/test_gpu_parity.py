@@ -30,7 +30,7 @@ def setup_module(module):
 
 SMALL = ["C0", "S_softmax", "S_sigmoid", "S_selected", "S_capgate", "S_cap3shared", "S_f32",
          "S_tied", "S_KeqN", "S_N1", "S_stream", "S_stream_cap", "S_rankcap", "S_rankcap_stream",
-         "S_wide", "S_wide192"]
+         "S_wide", "S_wide192", "S_longT"]
 _cache = {}
 
 
@@ -125,6 +125,42 @@ def test_permute_stage(name, copy_rows):
     xs = L.x[torch.from_numpy(perm.row_token).long().cuda()]
     assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
                        xs.view(torch.int16) if xs.dtype == torch.bfloat16 else xs.view(torch.int32))
+
+
+@pytest.mark.parametrize("copy_rows", [True, False])
+@pytest.mark.parametrize("T,group,budget", [(64 * 256, 0, 700), (64 * 257 + 5, 0, 700),
+                                            (64 * 257 + 5, 32, 9000)])
+def test_permute_histogram_sizes(T, group, budget, copy_rows):
+    """256 experts, top-8, Zipf-skewed and at capacity: 64 * 256 tokens give 65536
+    histogram entries (placement in one launch, each workgroup re-reading them all), one
+    more 64-token row (65792 entries) switches to the scan, then the map or row copy.
+    Kept counts, offsets, restoration map and rows bit-exact on both sides of the switch
+    ("Section 10", Eq. 21, 23, 25, 26)."""
+    N, K = 256, 8
+    say(f"permute T={T} N={N} K={K} group={group} budget={budget} copy_rows={copy_rows}")
+    rng = np.random.default_rng(T + group)
+    z = (rng.standard_normal((T, N)) + 2.0 * np.log(1.0 / np.arange(1, N + 1) ** 1.1)).astype(np.float32)
+    idx = O.topk_select(z, K)
+    xh = rng.standard_normal((T, 64)).astype(np.float32)
+    x = torch.from_numpy(xh).cuda().to(torch.bfloat16)
+    out = moe.moe_permute(x, torch.from_numpy(idx).cuda(), N, budget, copy_rows=copy_rows,
+                          capacity_group=group)
+    torch.cuda.synchronize()
+    if group > 0:
+        kept = O.keep_routes_rank_wide(idx, N, group, budget, n_sources=1)
+    else:
+        kept = O.keep_routes(idx, N, budget)
+    perm = O.permutation(idx, kept, N)
+    R = int(perm.offsets[-1])
+    assert R < T * K  # routes were dropped
+    assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, N))
+    assert np.array_equal(host(out["C_keep"]), perm.C_keep)
+    assert np.array_equal(host(out["offsets"]), perm.offsets)
+    assert np.array_equal(host(out["dest_row"]), perm.dest_row)
+    assert np.array_equal(host(out["row_token"])[:R], perm.row_token)
+    if copy_rows:
+        xs = x[torch.from_numpy(perm.row_token).long().cuda()]
+        assert torch.equal(out["x_perm"][:R].view(torch.int16), xs.view(torch.int16))
 
 
 @pytest.mark.parametrize("N,K,group,budget", [(64, 4, 8, 1500), (64, 4, 8, 0), (64, 4, 64, 9000),
