@@ -388,9 +388,137 @@ logits_split_kernel(int T, int d, int N, int kslice, const uint16_t* __restrict_
   }
 }
 
+
+// ---- phase 1, bf16, up to 128 logit columns: both operands staged through LDS ------------
+// The 16 x rows and the (padded) router rows of a k stage are brought into an LDS ring by
+// direct-to-LDS loads of whole row pieces (16-byte chunks XOR-swizzled by row), several
+// stages ahead, each load moving 1 KB of full row pieces; wave w then runs
+// v_mfma_f32_16x16x32_bf16 on k32 step (w mod KS) of each stage for every (8 / KS)-th
+// column block from LDS. The KS per-step partial tiles are added in a fixed order into
+// the logits tile.
+constexpr int LP_BT = 16;             // tokens per workgroup
+constexpr int LP_BK = 128;            // k per stage
+constexpr int LP_ROWB = LP_BK * 2;    // bytes per staged row piece
+constexpr int LP_CPR = LP_ROWB / 16;  // 16-byte chunks per row piece
+constexpr int LP_RPL = 64 / LP_CPR;   // row pieces per 1 KB load
+constexpr int LP_KS = LP_BK / 32;     // k32 steps per stage
+constexpr int LP_WPQ = 8 / LP_KS;     // waves per k32 step
+static_assert(LP_CPR >= 16 && LP_CPR <= 64 && LP_KS <= 8, "stage width");
+
+template <int NBT>
+struct LpCfg {
+  static constexpr int NC = NBT * 16;           // staged router rows (padded)
+  static constexpr int ROWS = LP_BT + NC;       // staged rows per stage
+  static constexpr int STAGE = ROWS * LP_ROWB;  // bytes per stage
+  static constexpr int NI = ROWS / LP_RPL;      // 1 KB loads per stage
+  static constexpr int M = (NI + 7) / 8;        // loads per wave per stage (8 waves)
+  static constexpr int S = NBT <= 4 ? 4 : 3;    // ring depth (stages)
+  static constexpr int WAITN = (S - 2) * M;     // loads still in flight when a stage starts
+  static constexpr int LDZ = NC + 1;
+  static constexpr int RING = S * STAGE;
+  static constexpr int NJ = (NBT + LP_WPQ - 1) / LP_WPQ;  // column blocks per wave
+  static_assert((LP_KS + 1) * LP_BT * LDZ * 4 <= RING, "partial tiles and logits fit the ring");
+  static_assert(WAITN < 64, "vmcnt range");
+};
+
+// bf16 logits of tokens t0 .. t0 + 15 into z = ring + KS partial tiles ([16][LDZ] floats,
+// columns < ncol valid); d a multiple of LP_BK; returns z
+template <int NBT>
+__device__ float* logits_lds(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                             const uint16_t* __restrict__ wgate, const float* __restrict__ logit_bias,
+                             int T, int d, int N, int NB, int ncol, int t0, char* ring) {
+  typedef LpCfg<NBT> C;
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nst = d / LP_BK;
+  const uint32_t ring_base = static_cast<uint32_t>((size_t)((lds_char*)ring));
+  // this lane's source of each of its M loads: load i = w + 8 u (past NI: load NI - 1
+  // again, the same bytes to the same place) brings staged rows RPL i .. RPL i + RPL - 1,
+  // lane l row RPL i + l / CPR, physical chunk l % CPR = logical chunk (l % CPR) ^ (row & 15)
+  const char* src[C::M];
+  uint32_t dst[C::M];
+#pragma unroll
+  for (int u = 0; u < C::M; ++u) {
+    const int i = min(w + 8 * u, C::NI - 1);
+    const int row = LP_RPL * i + lane / LP_CPR;
+    const int lc = (lane % LP_CPR) ^ (row & 15);
+    const uint16_t* rp;
+    if (row < LP_BT) {
+      rp = x + static_cast<size_t>(min(t0 + row, T - 1)) * d;
+    } else {
+      const int n = row - LP_BT;  // padding rows read router row 0; their columns are dropped
+      rp = n < N ? wr + static_cast<size_t>(n) * d : (n == N && wgate != nullptr ? wgate : wr);
+    }
+    src[u] = reinterpret_cast<const char*>(rp) + lc * 16;
+    dst[u] = ring_base + static_cast<uint32_t>(i) * 1024u;
+  }
+  // workgroup b walks the k stages from stage b mod nst (wrapping), so workgroups running
+  // side by side read different k ranges of W_r
+  const int skew = static_cast<int>(blockIdx.x % static_cast<unsigned>(nst));
+  auto issue = [&](int ks, int slot) {
+    const int kk = ks + skew < nst ? ks + skew : ks + skew - nst;
+#pragma unroll
+    for (int u = 0; u < C::M; ++u)
+      dma16(src[u] + static_cast<size_t>(kk) * LP_ROWB, dst[u] + slot * C::STAGE);
+  };
+  // operand LDS offset (within a stage) of this lane for its k32 step q
+  const int q = w % LP_KS, cb0 = w / LP_KS;
+  const int lr = lane & 15, lcq = q * 4 + (lane >> 4);
+  const uint32_t a_off = static_cast<uint32_t>(lr * LP_ROWB + ((lcq ^ lr) << 4));
+  floatx4 acc[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < C::S - 1; ++v) issue(min(v, nst - 1), v);
+  for (int s = 0; s < nst; ++s) {
+    wait_vmcnt<C::WAITN>();
+    __syncthreads();
+    // past the end: the last stage again into a slot no stage still needs
+    issue(min(s + C::S - 1, nst - 1), (s + C::S - 1) % C::S);
+    const char* st = ring + (s % C::S) * C::STAGE;
+    const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + a_off));
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+      const int nb = cb0 + LP_WPQ * j;
+      if (nb < NB) {
+        const bf16x8 bv = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(st + (LP_BT + 16 * nb) * LP_ROWB + a_off));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // the repeated last-stage loads too
+  __syncthreads();
+  // partial tile of k32 step q: lane holds column (lane & 15), rows 4 (lane >> 4) + j
+  float* part = reinterpret_cast<float*>(ring);
+  float* pq = part + q * LP_BT * C::LDZ;
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) {
+    const int nb = cb0 + LP_WPQ * j;
+    if (nb < NB) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pq[(4 * (lane >> 4) + e) * C::LDZ + nb * 16 + lr] = acc[j][e];
+    }
+  }
+  __syncthreads();
+  float* z = part + LP_KS * LP_BT * C::LDZ;
+  for (int i = tid; i < LP_BT * ncol; i += blockDim.x) {
+    const int t = i / ncol, n = i % ncol;
+    const int o = t * C::LDZ + n;
+    float v = part[o];  // fixed order: k32 steps 0, 1, ...
+#pragma unroll
+    for (int qq = 1; qq < LP_KS; ++qq) v += part[qq * LP_BT * C::LDZ + o];
+    if (n < N && logit_bias != nullptr) v += logit_bias[n];
+    z[o] = v;
+  }
+  return z;
+}
+
 // TILE_ONLY: logits come from memory (logits_mode 1 or 2), so LDS holds the one final
 // tile instead of a partial tile per wave
-template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false>
+// LDSP: bf16 logits by logits_lds (16 tokens, 8 waves), the tile and partials in its ring
+template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false, bool LDSP = false>
 __global__ void __launch_bounds__(WAVES * 64)
 route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
              const void* __restrict__ x, const void* __restrict__ w_router,
@@ -403,7 +531,11 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   constexpr int THREADS = WAVES * 64;
   static_assert(BT <= 32, "one 32-bit token mask per expert");
   constexpr int ldz = NBT * 16 + 1;
-  __shared__ float smem[(TILE_ONLY ? 1 : WAVES) * BT * ldz];  // bf16 path: a partial tile per wave
+  static_assert(!LDSP || (BT == LP_BT && WAVES == 8), "staged logits: 16 tokens, 8 waves");
+  // bf16 path: a partial tile per wave; TILE_ONLY: the one tile; staged path: the LDS ring
+  // (partials and tile in it)
+  __shared__ float smem[LDSP ? 1 : (TILE_ONLY ? 1 : WAVES) * BT * ldz];
+  __shared__ __attribute__((aligned(1024))) char ring[LDSP ? LpCfg<NBT>::RING : 16];
   float* z = smem;  // final logits tile [BT][ldz]
   const int t0 = blockIdx.x * BT;
   const int tid = threadIdx.x;
@@ -452,6 +584,10 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
     }
   } else if (TILE_ONLY) {
     return;  // not launched for logits computed here
+  } else if (LDSP) {
+    z = logits_lds<NBT>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                        static_cast<const uint16_t*>(w_gate_vec), logit_bias, T, d, N,
+                        (ncol + 15) / 16, ncol, t0, ring);
   } else if (dt == 1) {
     const int NB = (ncol + 15) / 16;
     logits_bf16<BT, NBT, WAVES, U>(static_cast<const uint16_t*>(x),
@@ -579,14 +715,14 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   }
 }
 
-template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false>
+template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false, bool LDSP = false>
 hipError_t launch_cfg(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
                       const void* x, const void* w_router, const float* logit_bias,
                       const float* sel_bias, const void* w_gate_vec, float* logits, int logits_mode, int32_t* topk_idx,
                       float* topk_r, float* s_tok, const float* part, int nparts,
                       int32_t* hist, int32_t* loc_rank, hipStream_t stream) {
   const int grid = (T + BT - 1) / BT;
-  hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U, TILE_ONLY>), dim3(grid), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((route_kernel<BT, NBT, WAVES, U, TILE_ONLY, LDSP>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      T, d, N, K, score, renorm, alpha, dt, x, w_router, logit_bias, sel_bias,
                      w_gate_vec,
                      logits, logits_mode, topk_idx, topk_r, s_tok, part, nparts, hist, loc_rank);
@@ -647,6 +783,20 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
                                           nullptr, logit_bias, expert_bias, nullptr, logits, 2,
                                           topk_idx, topk_r, nullptr, partials, P, hist, loc_rank,
                                           stream);
+  }
+  // bf16, 33 to 128 logit columns: the LDS-staged logits (with fewer columns the x rows
+  // dominate and the register-direct loads below stream them as fast)
+  if (dt == 1 && logits_mode == 0 && NB >= 3 && NB <= 8 && d_model % LP_BK == 0) {
+#define MOE_ROUTE_LDS(NBT_)                                                                  \
+  if (NB <= NBT_)                                                                            \
+    return launch_cfg<16, NBT_, 8, 1, false, true>(T, d_model, N, K, score, renorm, alpha,   \
+                                                   dt, x, w_router, logit_bias, expert_bias, \
+                                                   w_shared_gate, logits, logits_mode,       \
+                                                   topk_idx, topk_r, s_tok, nullptr, 0, hist, \
+                                                   loc_rank, stream);
+    MOE_ROUTE_LDS(4)
+    MOE_ROUTE_LDS(8)
+#undef MOE_ROUTE_LDS
   }
   // (tokens per workgroup, column blocks, waves, k steps in flight per wave): small N
   // uses 16 tokens and 8 waves; large N 32 tokens (router rows re-read half as often)
