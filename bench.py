@@ -14,8 +14,10 @@ Timing: W warm-up steps, then the K timed steps as K forward calls captured in o
 graph and replayed once between synchronizations (value, ms_per_step); beside it the
 same forward with one graph replay per step (mean over K, and the median of at least 50
 individually timed replays), and eager launches. Stage times are medians of 50 graph
-replays. --profile-forward N only replays the one-step graph N times, for a kernel trace
-of forward steps alone.
+replays, each replay holding several back-to-back calls (5 for the expert passes, 10 for
+the short stages) and timed per call, so that a replay's own launch and events stay out
+of one call's time. --profile-forward N only replays the one-step graph N times, for a
+kernel trace of forward steps alone.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ METRIC = "MoE fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 64e K=4"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_gemm_amd", "csrc", "gemm_stream.hip")
+GEMM_CALLS = 5  # expert-pass launches per timed graph replay
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "experts_gateup_olmo64e_traffic.json")
 
 
@@ -328,17 +331,21 @@ def main():
                                        lw["w_up"], lw["w_down"], shared=sm if with_shared else None,
                                        out=bufs, packed=pk, pass_=pass_)
     # the dominant kernel: the gate/up pass (routed experts + shared MLP, one launch), each
-    # replay timed with events on the stream it runs on; medians over `reps` replays
-    st["experts_gateup_ms"] = time_median(torch, experts(1), reps)
-    st["experts_down_ms"] = time_median(torch, experts(2), reps)
+    # replay timed with events on the stream it runs on; medians over `reps` replays of a
+    # graph of GEMM_CALLS back-to-back launches, per launch (as the forward runs them: a
+    # replay's own launch and events would otherwise enter one launch's time)
+    st["experts_gateup_ms"] = time_median(torch, experts(1), reps, calls=GEMM_CALLS)
+    st["experts_down_ms"] = time_median(torch, experts(2), reps, calls=GEMM_CALLS)
     # the same passes with the routed experts alone and the shared MLP alone
-    apart = {"routed_gateup_ms": time_median(torch, experts(1, False), reps),
-             "routed_down_ms": time_median(torch, experts(2, False), reps)}
+    apart = {"routed_gateup_ms": time_median(torch, experts(1, False), reps, calls=GEMM_CALLS),
+             "routed_down_ms": time_median(torch, experts(2, False), reps, calls=GEMM_CALLS)}
     if sm is not None:
         apart["shared_gateup_ms"] = time_median(torch, lambda: moe.moe_grouped_gemm(
-            x, None, sm[0][None], sm[1][None], out=bufs["h_shared"], swiglu=True, packed=pk), reps)
+            x, None, sm[0][None], sm[1][None], out=bufs["h_shared"], swiglu=True, packed=pk),
+            reps, calls=GEMM_CALLS)
         apart["shared_down_ms"] = time_median(torch, lambda: moe.moe_grouped_gemm(
-            bufs["h_shared"], None, sm[2][None], out=bufs["g"], swiglu=False, packed=pk), reps)
+            bufs["h_shared"], None, sm[2][None], out=bufs["g"], swiglu=False, packed=pk),
+            reps, calls=GEMM_CALLS)
     # shader clock while the gate/up pass replays back to back for about a second
     clock_mhz = gfx_clock_during(torch, capture(torch, experts(1)), 1.0)
     st["route_ms"] = time_median(torch, lambda: moe.moe_route(
@@ -473,9 +480,12 @@ def main():
         "shader_clock_mhz": None if clock_mhz is None else round(clock_mhz),
         "peak_bf16_at_clock_tflops": (None if clock_mhz is None else
                                       round(PEAK_BF16_TFLOPS * clock_mhz / 2400.0, 1)),
-        "stage_timing": f"median of {reps} graph replays per stage (route, permute, combine and "
-                        "the short next rows: 10 calls per replay)",
-        "roofline": dict(kernel=kernel_label, time="median of %d replays" % reps,
+        "stage_timing": f"median of {reps} graph replays per stage, per call (expert passes: "
+                        f"{GEMM_CALLS} calls per replay; route, permute, combine and the short "
+                        "next rows: 10)",
+        "roofline": dict(kernel=kernel_label,
+                         time="median of %d replays of %d back-to-back launches, per launch"
+                              % (reps, GEMM_CALLS),
                          **roof, algorithmic_bytes=bytes_gateup, flops_per_launch=flops_gateup,
                          mfma_tflops=round(flops_gateup / t_gateup / 1e12, 1),
                          mfma_frac=round(flops_gateup / t_gateup / 1e12 / PEAK_BF16_TFLOPS, 4)),
