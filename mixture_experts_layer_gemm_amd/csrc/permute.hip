@@ -231,6 +231,7 @@ constexpr int PL_TOK = 64;                // tokens placed per workgroup
 constexpr int PL_MAXP = 32;               // row runs per expert (reduced by one thread)
 constexpr int PL_ROWS = PL_TOK / 16;      // histogram rows per workgroup (rows of >= 16)
 constexpr int PL_PART = 4096;             // partial sums: runs x experts
+static_assert(PL_TOK * kMaxK <= PL_THREADS, "one route per thread");
 constexpr int kPlaceMaxHist = 64 * 1024;  // histogram entries each workgroup re-reads
 
 template <int V>
@@ -275,7 +276,12 @@ place_kernel(int T, int d, int N, int K, int R, int nrows, int capacity, int gro
   const int G = (N + V - 1) / V;
   const int P = min(PL_THREADS / G, PL_MAXP);
   const int g = tid % G, p = tid / G;
-  // this workgroup's own rows of expert tid, loaded up front with the runs' loads
+  // this thread's route (64 tokens x K <= 1024 threads: one each) and this workgroup's
+  // own rows of expert tid, loaded up front beside the runs' loads
+  const bool has_route = tid < ntok * K;
+  const size_t tk = static_cast<size_t>(tok0) * K + tid;
+  const int my_e = has_route ? topk_idx[tk] : 0;
+  const int my_rank = has_route ? loc_rank[tk] : 0;
   int own[PL_ROWS];
 #pragma unroll
   for (int ri = 0; ri < PL_ROWS; ++ri)
@@ -378,16 +384,14 @@ place_kernel(int T, int d, int N, int K, int R, int nrows, int capacity, int gro
     if (tid == 0) offsets[N] = s_scan[kMaxN - 1];
   }
   // 4. restoration map of this workgroup's routes
-  for (int i = tid; i < ntok * K; i += PL_THREADS) {
-    const size_t tk = static_cast<size_t>(tok0) * K + i;
-    const int t = tok0 + i / K;
-    const int e = topk_idx[tk];
-    const int rank = s_base[t / R - r0][e] + loc_rank[tk];
+  if (has_route) {
+    const int t = tok0 + tid / K;
+    const int rank = s_base[t / R - r0][my_e] + my_rank;
     int dest = -1;
-    if (rank < s_keep[e]) dest = s_scan[e] - s_keep[e] + rank;
+    if (rank < s_keep[my_e]) dest = s_scan[my_e] - s_keep[my_e] + rank;
     dest_row[tk] = dest;
     if (dest >= 0) row_token[dest] = t;
-    if constexpr (EB > 0) s_dest[i] = dest;
+    if constexpr (EB > 0) s_dest[tid] = dest;
   }
   // 5. row copy: wave w copies tokens w, w + 16, ... to their kept destinations
   if constexpr (EB > 0) {
