@@ -135,6 +135,16 @@ SMALL = {
     # places with a scan, then the map
     "S_longT": Config("small-many-tokens", 25, T=16400, d_model=256, N=64, K=4, d_r=128,
                       shared_widths=(64,), capacity_factor=1.0, zipf_bias=True, std_w=0.05),
+    # router shapes between the small and the many-expert ones: 40 experts + a gate column
+    # (three 16-column blocks) over a ragged last token tile; 100 experts (seven blocks,
+    # a three-stage LDS ring); 200 experts (not a multiple of 64: the register-direct
+    # 32-token router) with a gate and a d_model that is not a multiple of 128
+    "S_mid40": Config("small-40-experts-gate", 26, T=1001, d_model=384, N=40, K=5, d_r=128,
+                      shared_widths=(64,), shared_gate=True, capacity_factor=1.25, std_w=0.05),
+    "S_mid100": Config("small-100-experts", 27, T=555, d_model=640, N=100, K=6, d_r=192,
+                       score=SCORE_SIGMOID, alpha=2.0, std_w=0.04),
+    "S_mid200": Config("small-200-experts-gate", 28, T=300, d_model=320, N=200, K=8, d_r=128,
+                       shared_widths=(64,), shared_gate=True, std_w=0.04),
     "S_wide": Config("small-256-experts", 23, T=1000, d_model=1024, N=256, K=8, d_r=256,
                      shared_widths=(128,), score=SCORE_SIGMOID, alpha=2.5, std_w=0.03),
     # 192 experts (three groups of 64) under the Olmo rule, d_model in two slices

@@ -30,7 +30,7 @@ def setup_module(module):
 
 SMALL = ["C0", "S_softmax", "S_sigmoid", "S_selected", "S_capgate", "S_cap3shared", "S_f32",
          "S_tied", "S_KeqN", "S_N1", "S_stream", "S_stream_cap", "S_rankcap", "S_rankcap_stream",
-         "S_wide", "S_wide192", "S_longT"]
+         "S_wide", "S_wide192", "S_longT", "S_mid40", "S_mid100", "S_mid200"]
 _cache = {}
 
 
