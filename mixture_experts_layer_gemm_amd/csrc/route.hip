@@ -5,12 +5,15 @@
 // score rules, and the router projection of "Shared and Fine-Grained Experts" (a
 // bias-free linear layer from d_model to N).
 //
-// One workgroup owns BT tokens (16 with 8 waves for N <= 128, 32 with 4 waves beyond).
-// Phase 1 computes the BT x N logit tile: for bf16 with v_mfma_f32_16x16x32_bf16, the
-// d_model reduction split round-robin over the waves in 32-wide steps, operands loaded
-// straight from global memory into the MFMA lane layout several steps at a time (x is
-// streamed once; W_r stays in L2), and the per-wave partial tiles summed in LDS in a
-// fixed order. Phase 2 gives each wave BT / waves tokens: top-K by ranks of packed
+// One workgroup owns BT tokens. Phase 1 computes the BT x N logit tile in one of three
+// ways: for bf16 with 33 to 128 logit columns, 16 tokens and 16 waves with both operands
+// staged through an LDS ring (logits_lds); for 128 < N <= 256 without a gate, split-K
+// partial logits from a separate kernel (logits_split_kernel), added here in a fixed
+// order; otherwise (16 tokens and 8 waves up to 128 columns, 32 tokens and 4 waves
+// beyond) v_mfma_f32_16x16x32_bf16 with the d_model reduction split round-robin over the
+// waves in 32-wide steps, operands loaded straight from global memory into the MFMA lane
+// layout several steps at a time, and the per-wave partial tiles summed in LDS in a fixed
+// order. Phase 2 gives each wave BT / waves tokens: top-K by ranks of packed
 // (ordered float key, inverted expert index) 64-bit values, which put the lowest index
 // first on ties, then the coefficients in the lanes k < K. For N > 64 (several keys per
 // lane) the ranks are counted only among the keys at or above a threshold: the K-th
@@ -393,7 +396,7 @@ logits_split_kernel(int T, int d, int N, int kslice, const uint16_t* __restrict_
 // The 16 x rows and the (padded) router rows of a k stage are brought into an LDS ring by
 // direct-to-LDS loads of whole row pieces (16-byte chunks XOR-swizzled by row), several
 // stages ahead, each load moving 1 KB of full row pieces; wave w then runs
-// v_mfma_f32_16x16x32_bf16 on k32 step (w mod KS) of each stage for every (8 / KS)-th
+// v_mfma_f32_16x16x32_bf16 on k32 step (w mod KS) of each stage for every (WAVES / KS)-th
 // column block from LDS. The KS per-step partial tiles are added in a fixed order into
 // the logits tile.
 constexpr int LP_BT = 16;             // tokens per workgroup
@@ -402,45 +405,46 @@ constexpr int LP_ROWB = LP_BK * 2;    // bytes per staged row piece
 constexpr int LP_CPR = LP_ROWB / 16;  // 16-byte chunks per row piece
 constexpr int LP_RPL = 64 / LP_CPR;   // row pieces per 1 KB load
 constexpr int LP_KS = LP_BK / 32;     // k32 steps per stage
-constexpr int LP_WPQ = 8 / LP_KS;     // waves per k32 step
 static_assert(LP_CPR >= 16 && LP_CPR <= 64 && LP_KS <= 8, "stage width");
 
-template <int NBT>
+template <int NBT, int WAVES>
 struct LpCfg {
+  static constexpr int WPQ = WAVES / LP_KS;     // waves per k32 step
   static constexpr int NC = NBT * 16;           // staged router rows (padded)
   static constexpr int ROWS = LP_BT + NC;       // staged rows per stage
   static constexpr int STAGE = ROWS * LP_ROWB;  // bytes per stage
   static constexpr int NI = ROWS / LP_RPL;      // 1 KB loads per stage
-  static constexpr int M = (NI + 7) / 8;        // loads per wave per stage (8 waves)
+  static constexpr int M = (NI + WAVES - 1) / WAVES;  // loads per wave per stage
   static constexpr int S = NBT <= 4 ? 4 : 3;    // ring depth (stages)
   static constexpr int WAITN = (S - 2) * M;     // loads still in flight when a stage starts
   static constexpr int LDZ = NC + 1;
   static constexpr int RING = S * STAGE;
-  static constexpr int NJ = (NBT + LP_WPQ - 1) / LP_WPQ;  // column blocks per wave
+  static constexpr int NJ = (NBT + WPQ - 1) / WPQ;  // column blocks per wave
+  static_assert(WAVES % LP_KS == 0, "whole k32 steps per wave group");
   static_assert((LP_KS + 1) * LP_BT * LDZ * 4 <= RING, "partial tiles and logits fit the ring");
   static_assert(WAITN < 64, "vmcnt range");
 };
 
 // bf16 logits of tokens t0 .. t0 + 15 into z = ring + KS partial tiles ([16][LDZ] floats,
 // columns < ncol valid); d a multiple of LP_BK; returns z
-template <int NBT>
+template <int NBT, int WAVES>
 __device__ float* logits_lds(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                              const uint16_t* __restrict__ wgate, const float* __restrict__ logit_bias,
                              int T, int d, int N, int NB, int ncol, int t0, char* ring) {
-  typedef LpCfg<NBT> C;
+  typedef LpCfg<NBT, WAVES> C;
   typedef __attribute__((address_space(3))) char lds_char;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nst = d / LP_BK;
   const uint32_t ring_base = static_cast<uint32_t>((size_t)((lds_char*)ring));
-  // this lane's source of each of its M loads: load i = w + 8 u (past NI: load NI - 1
+  // this lane's source of each of its M loads: load i = w + WAVES u (past NI: load NI - 1
   // again, the same bytes to the same place) brings staged rows RPL i .. RPL i + RPL - 1,
   // lane l row RPL i + l / CPR, physical chunk l % CPR = logical chunk (l % CPR) ^ (row & 15)
   const char* src[C::M];
   uint32_t dst[C::M];
 #pragma unroll
   for (int u = 0; u < C::M; ++u) {
-    const int i = min(w + 8 * u, C::NI - 1);
+    const int i = min(w + WAVES * u, C::NI - 1);
     const int row = LP_RPL * i + lane / LP_CPR;
     const int lc = (lane % LP_CPR) ^ (row & 15);
     const uint16_t* rp;
@@ -480,7 +484,7 @@ __device__ float* logits_lds(const uint16_t* __restrict__ x, const uint16_t* __r
     const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + a_off));
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
-      const int nb = cb0 + LP_WPQ * j;
+      const int nb = cb0 + C::WPQ * j;
       if (nb < NB) {
         const bf16x8 bv = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(st + (LP_BT + 16 * nb) * LP_ROWB + a_off));
@@ -495,7 +499,7 @@ __device__ float* logits_lds(const uint16_t* __restrict__ x, const uint16_t* __r
   float* pq = part + q * LP_BT * C::LDZ;
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-    const int nb = cb0 + LP_WPQ * j;
+    const int nb = cb0 + C::WPQ * j;
     if (nb < NB) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) pq[(4 * (lane >> 4) + e) * C::LDZ + nb * 16 + lr] = acc[j][e];
@@ -517,7 +521,7 @@ __device__ float* logits_lds(const uint16_t* __restrict__ x, const uint16_t* __r
 
 // TILE_ONLY: logits come from memory (logits_mode 1 or 2), so LDS holds the one final
 // tile instead of a partial tile per wave
-// LDSP: bf16 logits by logits_lds (16 tokens, 8 waves), the tile and partials in its ring
+// LDSP: bf16 logits by logits_lds (16 tokens), the tile and partials in its ring
 template <int BT, int NBT, int WAVES, int U, bool TILE_ONLY = false, bool LDSP = false>
 __global__ void __launch_bounds__(WAVES * 64)
 route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int dt,
@@ -531,11 +535,11 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   constexpr int THREADS = WAVES * 64;
   static_assert(BT <= 32, "one 32-bit token mask per expert");
   constexpr int ldz = NBT * 16 + 1;
-  static_assert(!LDSP || (BT == LP_BT && WAVES == 8), "staged logits: 16 tokens, 8 waves");
+  static_assert(!LDSP || BT == LP_BT, "staged logits: 16 tokens");
   // bf16 path: a partial tile per wave; TILE_ONLY: the one tile; staged path: the LDS ring
   // (partials and tile in it)
   __shared__ float smem[LDSP ? 1 : (TILE_ONLY ? 1 : WAVES) * BT * ldz];
-  __shared__ __attribute__((aligned(1024))) char ring[LDSP ? LpCfg<NBT>::RING : 16];
+  __shared__ __attribute__((aligned(1024))) char ring[LDSP ? LpCfg<NBT, WAVES>::RING : 16];
   float* z = smem;  // final logits tile [BT][ldz]
   const int t0 = blockIdx.x * BT;
   const int tid = threadIdx.x;
@@ -585,7 +589,7 @@ route_kernel(int T, int d, int N, int K, int score, int renorm, float alpha, int
   } else if (TILE_ONLY) {
     return;  // not launched for logits computed here
   } else if (LDSP) {
-    z = logits_lds<NBT>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+    z = logits_lds<NBT, WAVES>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
                         static_cast<const uint16_t*>(w_gate_vec), logit_bias, T, d, N,
                         (ncol + 15) / 16, ncol, t0, ring);
   } else if (dt == 1) {
@@ -789,7 +793,7 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
   if (dt == 1 && logits_mode == 0 && NB >= 3 && NB <= 8 && d_model % LP_BK == 0) {
 #define MOE_ROUTE_LDS(NBT_)                                                                  \
   if (NB <= NBT_)                                                                            \
-    return launch_cfg<16, NBT_, 8, 1, false, true>(T, d_model, N, K, score, renorm, alpha,   \
+    return launch_cfg<16, NBT_, 16, 1, false, true>(T, d_model, N, K, score, renorm, alpha,  \
                                                    dt, x, w_router, logit_bias, expert_bias, \
                                                    w_shared_gate, logits, logits_mode,       \
                                                    topk_idx, topk_r, s_tok, nullptr, 0, hist, \
