@@ -56,15 +56,18 @@ def gemm_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc
-    summary, or None if absent or taken from a different version of the kernel."""
+    summary, or None if absent, taken on another workload or from a different version
+    of the kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha") != gemm_source_sha():
+        return None
+    if str(t.get("workload", "")).split(":")[0] != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -421,7 +424,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops_gateup / t_gateup / 1e12, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic()
+    roof["traffic"] = measured_traffic(cfg.name)
     stage_bytes = {
         "route": T * d * esz + N * d * esz + T * K * 8,
         # count: idx in, ranks out; map: idx + ranks in, dest_row + row_token out
