@@ -783,7 +783,7 @@ hipError_t launch_route(int T, int d_model, int N, int K, int score, int renorm,
                        reinterpret_cast<const uint16_t*>(wpk), partials);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_cfg<32, 17, 8, 1, true>(T, d_model, N, K, score, renorm, alpha, dt, nullptr,
+    return launch_cfg<32, 17, 16, 1, true>(T, d_model, N, K, score, renorm, alpha, dt, nullptr,
                                           nullptr, logit_bias, expert_bias, nullptr, logits, 2,
                                           topk_idx, topk_r, nullptr, partials, P, hist, loc_rank,
                                           stream);
