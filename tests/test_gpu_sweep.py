@@ -1,0 +1,95 @@
+"""Seeded sweeps over shapes for the integer stages, bit-exact against the oracle:
+moe_permute over expert counts 1..256, top-K up to 16, ragged token counts, both capacity
+policies and both sides of the one-launch placement limit; moe_route on given fp32 logits
+(all four score rules) with the router's own tile counts.
+("Section 10: Routing, Capacity, and Load Balancing", Eq. 19, 21, 23, 25, 26; "Appendix E",
+Table 52 for the score rules.)"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_layer_gemm_amd import moe
+from tests.gpu_common import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _selection(rng, T, N, K, skew):
+    z = rng.standard_normal((T, N)).astype(np.float32)
+    if skew:
+        z += (2.0 * np.log(1.0 / np.arange(1, N + 1) ** 1.1)).astype(np.float32)
+    return O.topk_select(z, K)
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 31, 40, 64, 100, 128, 129, 192, 200, 255, 256]))
+        K = int(rng.integers(1, min(16, N) + 1))
+        T = int(rng.choice([1, 7, 63, 64, 65, 333, 1000, 4097, 9001, 16453]))
+        pol = int(rng.integers(0, 3))  # 0 dropless, 1 per-expert, 2 rank-wide
+        divs = [g for g in range(1, N + 1) if N % g == 0]
+        group = int(rng.choice(divs)) if pol == 2 else 0
+        if pol == 0:
+            cap = -1
+        elif pol == 1:
+            cap = int(rng.integers(0, max(2, 2 * K * T // N)))
+        else:
+            cap = int(rng.integers(0, max(2, 2 * K * T * group // N)))
+        out.append((i, T, N, K, cap, group, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(40, 2024), ids=lambda c: f"c{c[0]}-T{c[1]}-N{c[2]}-K{c[3]}")
+def test_permute_sweep(case):
+    i, T, N, K, cap, group, skew, copy_rows = case
+    say(f"permute sweep {case}")
+    rng = np.random.default_rng(1000 + i)
+    idx = _selection(rng, T, N, K, skew)
+    x = torch.from_numpy(rng.standard_normal((T, 64)).astype(np.float32)).cuda().to(torch.bfloat16)
+    out = moe.moe_permute(x, torch.from_numpy(idx).cuda(), N, cap, copy_rows=copy_rows,
+                          capacity_group=group)
+    torch.cuda.synchronize()
+    kept = (O.keep_routes_rank_wide(idx, N, group, cap, n_sources=1) if group > 0
+            else O.keep_routes(idx, N, cap))
+    perm = O.permutation(idx, kept, N)
+    R = int(perm.offsets[-1])
+    assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, N))
+    assert np.array_equal(host(out["C_keep"]), perm.C_keep)
+    assert np.array_equal(host(out["offsets"]), perm.offsets)
+    assert np.array_equal(host(out["dest_row"]), perm.dest_row)
+    assert np.array_equal(host(out["row_token"])[:R], perm.row_token)
+    if copy_rows and R > 0:
+        xs = x[torch.from_numpy(perm.row_token).long().cuda()]
+        assert torch.equal(out["x_perm"][:R].view(torch.int16), xs.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", _cases(24, 77), ids=lambda c: f"c{c[0]}-T{c[1]}-N{c[2]}-K{c[3]}")
+def test_route_counts_sweep(case):
+    """Top-K, coefficients and C^req from given logits: the router counts its own tiles
+    (16 or 32 tokens) and C^req is their per-expert sum."""
+    i, T, N, K, _, _, skew, _ = case
+    score = i % 4
+    renorm = score != 2 and (i // 4) % 2 == 0
+    rng = np.random.default_rng(5000 + i)
+    z = (rng.integers(-8, 9, size=(T, N)) * 0.25).astype(np.float32)  # many exact ties
+    z[::3] = rng.standard_normal((len(z[::3]), N)).astype(np.float32)
+    if skew:
+        z += (2.0 * np.log(1.0 / np.arange(1, N + 1) ** 1.1)).astype(np.float32)
+    sc = [O.SOFTMAX, O.SIGMOID, O.SOFTMAX_SELECTED, O.SOFTMAX][score]
+    say(f"route sweep {case} score {sc} renorm {renorm}")
+    out = moe.moe_route(None, None, K, score=sc, renorm=renorm, alpha=1.5,
+                        logits=torch.from_numpy(z).cuda(), logits_mode=1, want_counts=True)
+    torch.cuda.synchronize()
+    idx = O.topk_select(z, K)
+    assert np.array_equal(host(out["topk_idx"]), idx)
+    assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, N))
+    r = O.route_coefficients(z.astype(np.float64), idx, sc, renorm, 1.5)
+    assert np.max(np.abs(host(out["topk_r"]) - r)) <= 1e-4
