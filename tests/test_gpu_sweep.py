@@ -93,3 +93,41 @@ def test_route_counts_sweep(case):
     assert np.array_equal(host(out["C_req"]), O.requested_counts(idx, N))
     r = O.route_coefficients(z.astype(np.float64), idx, sc, renorm, 1.5)
     assert np.max(np.abs(host(out["topk_r"]) - r)) <= 1e-4
+
+
+def _layer_cases(n, seed):
+    from mixture_experts_layer_gemm_amd import synth
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 33, 48, 64]))
+        K = int(rng.integers(1, min(8, N) + 1))
+        d = int(rng.choice([64, 128, 256, 512, 768, 1024]))
+        d_r = int(rng.choice([64, 128, 256, 512, 768]))
+        ns = int(rng.integers(0, 3))
+        widths = tuple(int(rng.choice([64, 128, 256, 512])) for _ in range(ns))
+        score = int(rng.integers(0, 3))
+        cf = [None, None, 0.5, 1.0, 1.5][int(rng.integers(0, 5))]
+        divs = [g for g in range(2, N + 1) if N % g == 0]
+        group = int(rng.choice(divs)) if (cf is not None and divs and rng.integers(0, 3) == 0) else 0
+        cfg = synth.Config(
+            f"sweep-{i}", 200 + i, T=int(rng.choice([1, 5, 64, 129, 300, 777])), d_model=d, N=N,
+            K=K, d_r=d_r, shared_widths=widths, score=score, renorm=bool(rng.integers(0, 2)),
+            alpha=float(rng.choice([1.0, 2.5, K])), s=float(rng.choice([1.0, 0.5])),
+            capacity_factor=cf, capacity_group=group,
+            dtype="f32" if rng.integers(0, 6) == 0 else "bf16",
+            std_w=float(rng.uniform(0.5, 2.0) / np.sqrt(d)), zipf_bias=bool(rng.integers(0, 2)),
+            shared_gate=bool(ns > 0 and rng.integers(0, 2)))
+        out.append(cfg)
+    return out
+
+
+@pytest.mark.parametrize("cfg", _layer_cases(32, 31), ids=lambda c: c.name)
+def test_forward_sweep(cfg):
+    """Whole small layers of seeded random shapes against the whole-layer oracle: routing
+    bit-exact, every expert's H and F segment, G and y within the dtype's bound."""
+    from tests.gpu_common import DeviceLayer
+    from tests.test_gpu_parity import check_forward, setup_module as parity_setup
+    parity_setup(None)
+    say(f"forward sweep {cfg}")
+    check_forward(DeviceLayer(cfg), full=True)
