@@ -131,3 +131,13 @@ def test_forward_sweep(cfg):
     parity_setup(None)
     say(f"forward sweep {cfg}")
     check_forward(DeviceLayer(cfg), full=True)
+
+
+@pytest.mark.parametrize("cfg", [c for c in _layer_cases(32, 31) if c.dtype == "bf16"][:16],
+                         ids=lambda c: c.name)
+def test_backward_sweep(cfg):
+    """The fixed-router backward of the same random bf16 layers against the oracle's."""
+    import tests.test_gpu_backward as B
+    from tests.gpu_common import DeviceLayer
+    B.setup_module(None)
+    B.check_backward(DeviceLayer(cfg))
