@@ -190,7 +190,8 @@ def cpu_baseline(inp, sample_tokens: int):
     cap = -1 if c.capacity_factor is None else O.capacity_from_factor(c.capacity_factor, c.K, sample_tokens, c.N)
     spec = O.LayerSpec(N=c.N, K=c.K, score=c.score, renorm=c.renorm, alpha=c.alpha, s=c.s, capacity=cap)
     times = []
-    while len(times) < 3 and sum(times) < 10.0:
+    # at least 3 runs and about 10 s of oracle work in all (at most 15 runs)
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 15):
         t0 = time.perf_counter()
         O.forward(spec, x, inp.as_float(inp.w_router), inp.expert_f32, inp.shared_f32(),
                   logit_bias=inp.logit_bias,
