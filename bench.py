@@ -17,7 +17,8 @@ individually timed replays), and eager launches. Stage times are medians of 50 g
 replays, each replay holding several back-to-back calls (5 for the expert passes, 10 for
 the short stages) and timed per call, so that a replay's own launch and events stay out
 of one call's time. --profile-forward N only replays the one-step graph N times, for a
-kernel trace of forward steps alone.
+kernel trace of forward steps alone; --profile-backward N does the same for the
+fixed-router backward.
 """
 from __future__ import annotations
 
@@ -212,6 +213,9 @@ def main():
     ap.add_argument("--workload", default="C1")
     ap.add_argument("--stage-reps", type=int, default=50,
                     help="timed replays per stage (the median is reported)")
+    ap.add_argument("--profile-backward", type=int, default=0, metavar="N",
+                    help="only replay a captured fixed-router backward N times after one forward "
+                         "(bf16 workloads; for a kernel trace of backward calls alone)")
     ap.add_argument("--profile-forward", type=int, default=0, metavar="N",
                     help="only replay the captured forward N times after the warmup (for a "
                          "kernel trace of forward steps alone) and print one timing line")
@@ -265,6 +269,25 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
+
+    if args.profile_backward > 0:
+        if dt != "bf16":
+            print("the backward is bf16 only", file=sys.stderr)
+            sys.exit(2)
+        layer_t = moe.MoELayer(x, w_router, w_gate, w_up, w_down, K, score=cfg.score,
+                               renorm=cfg.renorm, alpha=cfg.alpha, s=cfg.s, capacity=cap,
+                               logit_bias=bias, w_shared_gate=gate, shared=shared, trainable=True)
+        layer_t.forward()
+        dy = torch.randn(T, d, device=x.device, dtype=torch.float32).to(torch.bfloat16)
+        gb = capture(torch, lambda: layer_t.backward(dy))
+        for _ in range(args.warmup):
+            gb.replay()
+        torch.cuda.synchronize()
+        t = replay_times(torch, gb, args.profile_backward)
+        print(json.dumps({"mode": "backward graph replays only", "workload": cfg.name,
+                          "replays": len(t), "ms_median": round(float(np.median(t)), 4),
+                          "ms_mean": round(float(np.mean(t)), 4)}), flush=True)
+        return
 
     # the forward captured once in a HIP graph; each step is one replay
     s = torch.cuda.Stream()
