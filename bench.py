@@ -59,8 +59,8 @@ def gemm_source_sha() -> str:
 
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc
-    summary, or None if absent, taken on another workload or from a different version
-    of the kernel."""
+    summary, or None if absent, taken on another workload (name and shapes, as the bench
+    line labels it) or from a different version of the kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -68,7 +68,7 @@ def measured_traffic(workload: str):
         return None
     if t.get("kernel_source_sha") != gemm_source_sha():
         return None
-    if str(t.get("workload", "")).split(":")[0] != workload:
+    if str(t.get("workload", "")).split(",")[0].strip() != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -124,7 +124,8 @@ def cpu_model() -> str:
 
 def gfx_clock_during(torch, g, seconds: float):
     """Median shader (GFX) clock in MHz sampled through amdsmi while graph g replays
-    back to back for about `seconds`; None where amdsmi is not available."""
+    back to back for about `seconds`, over the samples taken while the GPU was busy;
+    None where amdsmi is not available or too few samples were."""
     import threading
     try:
         import amdsmi
@@ -156,7 +157,12 @@ def gfx_clock_during(torch, g, seconds: float):
     except Exception:
         pass
     keep = samples[len(samples) // 5:]  # drop the ramp at the start of the window
-    return float(np.median(keep)) if keep else None
+    # samples taken while the GPU sat idle between replays read the idle clock: keep the
+    # busy ones (within half of the highest reading)
+    if keep:
+        top = max(keep)
+        keep = [c for c in keep if c >= 0.5 * top]
+    return float(np.median(keep)) if len(keep) >= 5 else None
 
 
 def time_cold(torch, fn, reps: int, scratch) -> float:
@@ -201,7 +207,7 @@ def cpu_baseline(inp, sample_tokens: int):
     dt = float(np.median(times))
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"{sample_tokens} of {c.T} tokens of the same layer (all {c.N} experts), fp64 "
+            "sample": f"{sample_tokens} of {inp.x.shape[0]} tokens of the same layer (all {c.N} experts), fp64 "
                       f"NumPy forward only, median of {len(times)} runs of {dt:.1f} s"}
 
 
@@ -211,6 +217,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C1")
+    ap.add_argument("--tokens", type=int, default=0, metavar="T",
+                    help="run the workload's layer on T tokens instead of its own count "
+                         "(the workload label names T)")
     ap.add_argument("--stage-reps", type=int, default=50,
                     help="timed replays per stage (the median is reported)")
     ap.add_argument("--profile-backward", type=int, default=0, metavar="N",
@@ -237,7 +246,10 @@ def main():
     from mixture_experts_layer_gemm_amd import moe
 
     cfg = synth.get_config(args.workload)
-    log(f"generating {cfg.name} inputs ...")
+    if args.tokens > 0:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, T=args.tokens)
+    log(f"generating {cfg.name} inputs (T={cfg.T}) ...")
     t0 = time.time()
     inp = synth.make_inputs(cfg)
     log(f"  {time.time() - t0:.1f} s; uploading")
@@ -249,6 +261,7 @@ def main():
     bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).cuda()
     gate = None if inp.w_shared_gate is None else to_device(inp.w_shared_gate, dt, torch)
     T, d, N, K, d_r = cfg.T, cfg.d_model, cfg.N, cfg.K, cfg.d_r
+    workload_label = f"{cfg.name}: T={T} d_model={d} N={N} K={K} d_r={d_r} d_s={cfg.d_s}"
     cap = moe.capacity_from_factor(cfg.capacity_factor, K, T, N) if cfg.capacity_factor is not None else -1
     layer = moe.MoELayer(x, w_router, w_gate, w_up, w_down, K, score=cfg.score, renorm=cfg.renorm,
                          alpha=cfg.alpha, s=cfg.s, capacity=cap, logit_bias=bias, w_shared_gate=gate,
@@ -448,7 +461,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops_gateup / t_gateup / 1e12, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(cfg.name)
+    roof["traffic"] = measured_traffic(workload_label)
     stage_bytes = {
         "route": T * d * esz + N * d * esz + T * K * 8,
         # count: idx in, ranks out; map: idx + ranks in, dest_row + row_token out
@@ -490,7 +503,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dt == "bf16" else "f32",
         "data": "synthetic: seeded normals (x ~ N(0,1), weights ~ N(0, %g)), bf16-rounded" % cfg.std_w,
-        "config": {"workload": f"{cfg.name}: T={T} d_model={d} N={N} K={K} d_r={d_r} d_s={cfg.d_s}",
+        "config": {"workload": workload_label,
                    "T": T, "d_model": d, "N": N, "K": K, "d_r": d_r, "d_s": cfg.d_s,
                    "score": ["softmax", "sigmoid", "softmax_selected"][cfg.score],
                    "renorm": cfg.renorm, "alpha": cfg.alpha, "capacity": cap,

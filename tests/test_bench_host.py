@@ -20,14 +20,15 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_only_for_its_workload_and_kernel_source(tmp_path, monkeypatch):
-    c1 = synth.get_config("C1").name
-    rec = {"kernel_source_sha": bench.gemm_source_sha(), "workload": f"{c1}: T=4096",
+    c1 = "olmo-64e-top4: T=4096 d_model=2048 N=64 K=4 d_r=2560 d_s=1280"
+    rec = {"kernel_source_sha": bench.gemm_source_sha(), "workload": f"{c1}, 16384 kept routes",
            "hbm_bytes_per_launch": 123}
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.measured_traffic(c1) == 123
-    assert bench.measured_traffic(synth.get_config("C4A").name) is None
+    assert bench.measured_traffic(c1.replace("T=4096", "T=8192")) is None
+    assert bench.measured_traffic(c1.replace("olmo-64e-top4", "skewed-capacity-qwen-gate")) is None
     f.write_text(json.dumps(dict(rec, kernel_source_sha="0" * 16)))
     assert bench.measured_traffic(c1) is None
     f.write_text("not json")
